@@ -1,0 +1,157 @@
+/*
+ * q8narrow.h -- narrow-batch q8_0 decode matmul for AMD Instinct MI355X
+ * (gfx950): the C ABI.
+ *
+ * The operation.  "Batched decode: co-decode N live sessions in one GPU pass"
+ * (antirez/ds4 PR #530), section "Why it's worth it -- the narrow-batch
+ * matmul", and its commit "CUDA: narrow-batch q8_0 matmul for 2-4 token
+ * decode": in memory-bound decode, a weight matrix stored as q8_0 blocks of
+ * 32 weights is read from memory once per step and each block is dotted
+ * against the pre-quantised activation blocks of every live token.  For a live
+ * batch of n_live tokens gathered through batch_index from a fixed buffer of
+ * 16 activation slots ("[feature] Enable Dynamic Batching" (quic/
+ * efficient-transformers PR #1305), section "Objective"; "dynamic public
+ * batch (1..16) for Qwen3-14B decode" (hw-native-sys/pypto-lib PR #841),
+ * commit message: the live batch 1..16 against a fixed padded width):
+ *
+ *     S[t,n,b] = sum_{i<32} qw[n,32b+i] * qx[batch_index[t],32b+i]  (int32)
+ *     Y[t,n]   = sum_b S[t,n,b] * dw[n,b] * dx[batch_index[t],b]     (fp32)
+ *
+ * q8_0 block (the pages name it but do not spell it out; this is the GGUF
+ * reading): 32 int8 values and one binary16 scale d = absmax/127, with
+ * q = clamp(round_half_away(x/d), -127, 127) using the binary32 d and IEEE
+ * division; an all-zero block stores d = +0 and q = 0.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named W, X, Y, Wq, Xq, q, d16, batch_index are DEVICE
+ *     pointers owned by the caller; the library allocates nothing and keeps
+ *     no state beyond cached device properties.
+ *   - Work is enqueued on `stream` (0 = the null stream) and is asynchronous:
+ *     no host synchronisation happens inside any call.  Calls are
+ *     thread-safe; calls that write the same buffer must be ordered by the
+ *     caller.
+ *   - Arguments are validated on the host before any HIP call; a rejected
+ *     call returns Q8_ERR_INVALID_ARG and enqueues nothing.  A device that
+ *     is not gfx950 gives Q8_ERR_UNSUPPORTED; a launch failure reported by
+ *     the HIP runtime gives Q8_ERR_HIP.  The library never aborts.
+ *   - Shapes: N >= 1 output features, K >= 32 input features with K % 32 == 0,
+ *     N * K <= 2^40, K < 2^24.
+ *   - Alignment: W, X, Wq, Xq 16 bytes; q 8 bytes; Y, batch_index 4 bytes;
+ *     d16 2 bytes.  A null or misaligned pointer is an invalid argument.
+ */
+#ifndef Q8NARROW_H
+#define Q8NARROW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q8_BLOCK 32     /* values per q8_0 block */
+#define Q8_MAX_SLOTS 16 /* activation slots in the padded buffer */
+
+typedef enum q8_status {
+    Q8_OK = 0,
+    Q8_ERR_INVALID_ARG = 1,
+    Q8_ERR_UNSUPPORTED = 2,
+    Q8_ERR_HIP = 3
+} q8_status;
+
+/* Which int8 dot engine the matmul uses (all give bit-identical Y). */
+typedef enum q8_path {
+    Q8_PATH_AUTO = 0, /* the library's choice (matrix cores) */
+    Q8_PATH_MFMA = 1, /* v_mfma_i32_16x16x32_i8: 16 rows x 16 tokens per block */
+    Q8_PATH_DOT4 = 2  /* v_dot4 int8 dot products, one row per lane */
+} q8_path;
+
+/* ------------------------------------------------------------------ sizes */
+
+/* Bytes of the packed weight buffer for an N x K matrix; 0 if the shape is
+ * invalid.  The packed layout is private to the library (it is tiled for
+ * the matmul kernels); use q8_unpack_weights to read it back. */
+size_t q8_packed_weight_bytes(int64_t N, int64_t K);
+
+/* Bytes between consecutive activation slots for K inputs; 0 if invalid.
+ *
+ * Activation slot buffer layout (public): Q8_MAX_SLOTS slots; slot s starts
+ * at byte s * stride and holds int8 q[Kp] followed by binary16 d[Kp/32],
+ * where Kp is K rounded up to a multiple of 256.  Entries at and beyond K
+ * (resp. K/32) are padding: q8_quantize_acts writes them as zero and the
+ * matmul never uses them.  stride is a multiple of 256 bytes. */
+size_t q8_act_slot_stride(int64_t K);
+
+/* Bytes of a whole activation slot buffer: Q8_MAX_SLOTS * stride. */
+size_t q8_act_buffer_bytes(int64_t K);
+
+/* -------------------------------------------------------------- packing */
+
+/* Quantise fp32 weights W [N][K] (row-major) to q8_0 and
+ * write them in the packed layout to Wq (q8_packed_weight_bytes(N, K)
+ * bytes).  Offline, once per matrix.
+ * Same quantisation rule as above, bit-exact with the definition. */
+q8_status q8_pack_weights(const float* W, int64_t N, int64_t K, void* Wq,
+                          hipStream_t stream);
+
+/* Pack already-quantised canonical q8_0 weights: q int8 [N][K] and d16
+ * binary16 bits [N][K/32], both row-major.  Any int8 value, -128 included,
+ * and any finite scale are accepted. */
+q8_status q8_pack_weights_q(const int8_t* q, const uint16_t* d16, int64_t N,
+                            int64_t K, void* Wq, hipStream_t stream);
+
+/* Read a packed buffer back into canonical q [N][K] and d16 [N][K/32]. */
+q8_status q8_unpack_weights(const void* Wq, int64_t N, int64_t K, int8_t* q,
+                            uint16_t* d16, hipStream_t stream);
+
+/* --------------------------------------------------------- activations */
+
+/* Pre-quantise activations ("preq"; same page, same section): fp32 rows
+ * X [n_rows][K] (row-major) go to slots 0..n_rows-1 of the slot buffer Xq,
+ * block by block with the q8_0 rule.
+ * Slots n_rows..15 are left untouched.  1 <= n_rows <= Q8_MAX_SLOTS. */
+q8_status q8_quantize_acts(const float* X, int n_rows, int64_t K, void* Xq,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------- matmul */
+
+/* Y[t][n] for t < n_live, n < N (fp32, row-major [n_live][N], overwritten,
+ * 4-byte aligned).  Wq: packed weights of the N x K matrix.  Xq: an
+ * activation slot buffer for K.  batch_index: int32 [n_live] device array;
+ * token t uses slot batch_index[t]; entries may repeat and come in any
+ * order.  1 <= n_live <= Q8_MAX_SLOTS.
+ *
+ * Each weight block is read from memory once per call and used for every
+ * live token.  The fp32 summation order depends only on (N, K), never on
+ * n_live or on the other tokens, so row t of Y is bit-identical to a call
+ * with n_live = 1 and batch_index = {batch_index[t]}.
+ *
+ * A batch_index entry outside [0, 16) cannot be checked on the host without
+ * a synchronisation; it is not read through: that token's row of Y is set
+ * to quiet NaN. */
+q8_status q8_matmul_narrow(const void* Wq, const void* Xq,
+                           const int32_t* batch_index, int n_live, int64_t N,
+                           int64_t K, float* Y, hipStream_t stream);
+
+/* As q8_matmul_narrow, with an explicit choice of int8 dot engine (for
+ * comparing the two; both give bit-identical results). */
+q8_status q8_matmul_narrow_path(const void* Wq, const void* Xq,
+                                const int32_t* batch_index, int n_live,
+                                int64_t N, int64_t K, float* Y,
+                                hipStream_t stream, q8_path path);
+
+/* ---------------------------------------------------------------- misc */
+
+/* 1 if the current HIP device is gfx950, 0 if not or if none is usable. */
+int q8_device_supported(void);
+
+/* A static string naming a status code. */
+const char* q8_status_str(q8_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8NARROW_H */

@@ -1,0 +1,145 @@
+// q8_abi.hip -- the extern "C" entry points of libq8narrow.so (see
+// include/q8narrow.h for the contract).
+//
+// Every entry point validates its arguments on the host before making any
+// HIP call, in the spirit of "[feature] Enable Dynamic Batching", section
+// "Assumptions and limitations" (reject an invalid combination early with a
+// clear error) and of "dynamic public batch (1..16) for Qwen3-14B decode",
+// commit message (the live batch must satisfy 1 <= batch <= pad).  Then it
+// checks the device (gfx950 only) and enqueues kernels on the caller's
+// stream.  Nothing is allocated and nothing synchronises.
+
+#include "q8narrow.h"
+#include "q8_internal.h"
+
+#include <atomic>
+#include <cstring>
+
+namespace {
+
+constexpr int64_t kMaxK = int64_t(1) << 24;
+constexpr int64_t kMaxNK = int64_t(1) << 40;
+
+bool valid_shape(int64_t N, int64_t K) {
+    return N >= 1 && K >= Q8_BLOCK && K % Q8_BLOCK == 0 && K < kMaxK &&
+           N <= kMaxNK / K;
+}
+
+bool aligned(const void* p, uintptr_t a) {
+    return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+// Per-device cache of "is this a gfx950": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int current_device_ok() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices) {
+        const int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+        if (c) return c == 1;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+    const int ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                   (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':');
+    if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok;
+}
+
+q8_status from_hip(hipError_t e) { return e == hipSuccess ? Q8_OK : Q8_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t q8_packed_weight_bytes(int64_t N, int64_t K) {
+    if (!valid_shape(N, K)) return 0;
+    const q8::Shape s = q8::make_shape(N, K);
+    return (size_t)(s.q_bytes + s.d_bytes);
+}
+
+size_t q8_act_slot_stride(int64_t K) {
+    if (!valid_shape(1, K)) return 0;
+    return (size_t)q8::make_shape(1, K).stride;
+}
+
+size_t q8_act_buffer_bytes(int64_t K) {
+    return (size_t)Q8_MAX_SLOTS * q8_act_slot_stride(K);
+}
+
+q8_status q8_pack_weights(const float* W, int64_t N, int64_t K, void* Wq,
+                          hipStream_t stream) {
+    if (!valid_shape(N, K) || !aligned(W, 16) || !aligned(Wq, 16)) return Q8_ERR_INVALID_ARG;
+    if (!current_device_ok()) return Q8_ERR_UNSUPPORTED;
+    const q8::Shape s = q8::make_shape(N, K);
+    return from_hip(q8::launch_pack_weights(W, s, static_cast<uint8_t*>(Wq), stream));
+}
+
+q8_status q8_pack_weights_q(const int8_t* q, const uint16_t* d16, int64_t N,
+                            int64_t K, void* Wq, hipStream_t stream) {
+    if (!valid_shape(N, K) || !aligned(q, 8) || !aligned(d16, 2) || !aligned(Wq, 16))
+        return Q8_ERR_INVALID_ARG;
+    if (!current_device_ok()) return Q8_ERR_UNSUPPORTED;
+    const q8::Shape s = q8::make_shape(N, K);
+    return from_hip(q8::launch_pack_weights_q(q, d16, s, static_cast<uint8_t*>(Wq), stream));
+}
+
+q8_status q8_unpack_weights(const void* Wq, int64_t N, int64_t K, int8_t* q,
+                            uint16_t* d16, hipStream_t stream) {
+    if (!valid_shape(N, K) || !aligned(Wq, 16) || !aligned(q, 8) || !aligned(d16, 2))
+        return Q8_ERR_INVALID_ARG;
+    if (!current_device_ok()) return Q8_ERR_UNSUPPORTED;
+    const q8::Shape s = q8::make_shape(N, K);
+    return from_hip(q8::launch_unpack_weights(static_cast<const uint8_t*>(Wq), s, q, d16, stream));
+}
+
+q8_status q8_quantize_acts(const float* X, int n_rows, int64_t K, void* Xq,
+                           hipStream_t stream) {
+    if (!valid_shape(1, K) || n_rows < 1 || n_rows > Q8_MAX_SLOTS || !aligned(X, 16) ||
+        !aligned(Xq, 16))
+        return Q8_ERR_INVALID_ARG;
+    if (!current_device_ok()) return Q8_ERR_UNSUPPORTED;
+    const q8::Shape s = q8::make_shape(1, K);
+    return from_hip(q8::launch_quantize_acts(X, n_rows, s, static_cast<uint8_t*>(Xq), stream));
+}
+
+q8_status q8_matmul_narrow_path(const void* Wq, const void* Xq,
+                                const int32_t* batch_index, int n_live,
+                                int64_t N, int64_t K, float* Y,
+                                hipStream_t stream, q8_path path) {
+    if (!valid_shape(N, K) || n_live < 1 || n_live > Q8_MAX_SLOTS || !aligned(Wq, 16) ||
+        !aligned(Xq, 16) || !aligned(batch_index, 4) || !aligned(Y, 4))
+        return Q8_ERR_INVALID_ARG;
+    if (path != Q8_PATH_AUTO && path != Q8_PATH_MFMA && path != Q8_PATH_DOT4)
+        return Q8_ERR_INVALID_ARG;
+    if (!current_device_ok()) return Q8_ERR_UNSUPPORTED;
+    const q8::Shape s = q8::make_shape(N, K);
+    const q8::Tiling t = q8::choose_tiling(s);
+    const q8::Engine e = path == Q8_PATH_DOT4 ? q8::Engine::kDot4 : q8::Engine::kMfma;
+    return from_hip(q8::launch_matmul(e, static_cast<const uint8_t*>(Wq),
+                                      static_cast<const uint8_t*>(Xq), batch_index,
+                                      n_live, s, t, Y, stream));
+}
+
+q8_status q8_matmul_narrow(const void* Wq, const void* Xq,
+                           const int32_t* batch_index, int n_live, int64_t N,
+                           int64_t K, float* Y, hipStream_t stream) {
+    return q8_matmul_narrow_path(Wq, Xq, batch_index, n_live, N, K, Y, stream,
+                                 Q8_PATH_AUTO);
+}
+
+int q8_device_supported(void) { return current_device_ok(); }
+
+const char* q8_status_str(q8_status status) {
+    switch (status) {
+        case Q8_OK: return "Q8_OK";
+        case Q8_ERR_INVALID_ARG: return "Q8_ERR_INVALID_ARG";
+        case Q8_ERR_UNSUPPORTED: return "Q8_ERR_UNSUPPORTED";
+        case Q8_ERR_HIP: return "Q8_ERR_HIP";
+    }
+    return "Q8_ERR_UNKNOWN";
+}
+
+}  // extern "C"

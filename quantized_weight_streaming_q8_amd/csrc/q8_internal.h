@@ -1,0 +1,144 @@
+// q8_internal.h -- layouts and launch helpers shared by the q8narrow kernels.
+//
+// Packed weight layout (private).  The matrix is cut into row groups of 16
+// rows (the N side of one v_mfma_i32_16x16x32_i8) and, along K, into
+// super-chunks of 8 q8_0 blocks (256 values); a super-chunk is 4 chunks of 2
+// blocks.  G = ceil(N/16) row groups, NSC = ceil(K/256) super-chunks; rows and
+// blocks past the matrix are zero (q = 0, d = 0).
+//
+//   q region, 4096 bytes per (group, super-chunk), groups outermost:
+//     byte ((g*NSC + sc)*4 + c)*1024 + lane*16 + h*8 + e
+//       = q[row 16g + (lane & 15)][k = 32*(8sc + 2c + h) + P(lane >> 4) + e]
+//     with P = {0, 16, 8, 24}.  One 16-byte load per lane of a wave64 then
+//     holds this lane's 8-byte B operand of the MFMA for block 2c (h = 0) and
+//     block 2c+1 (h = 1): row = lane & 15, k-slot = lane >> 4.
+//   scale region, after the q region, 256 bytes per (group, super-chunk):
+//     half ((g*NSC + sc)*16 + j)*8 + bb = d[row 16g + j][block 8sc + bb]
+//
+// The permutation P follows from how the activation operand is built: lane
+// (token t, k-slot s) loads 16 contiguous bytes of token t's canonical slot at
+// 64c + 16s (s = 0,1 hold block 2c, s = 2,3 block 2c+1) and one
+// v_permlane32_swap exchanges 8 bytes between lanes l and l+32, after which
+// lane slot s holds bytes P(s)..P(s)+7 of both blocks.  Any permutation is
+// exact here, since a block's 32 products are summed in integers.
+//
+// Activation slot buffer (public, see q8narrow.h): slot s at s*stride holds
+// int8 q[Kp] then binary16 d[Kp/32], Kp = 256*NSC.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8 {
+
+constexpr int kBlock = 32;        // values per q8_0 block
+constexpr int kMaxSlots = 16;     // activation slots
+constexpr int kRowsPerGroup = 16; // rows per row group
+constexpr int kScBlocks = 8;      // blocks per super-chunk
+constexpr int kScValues = kScBlocks * kBlock;            // 256
+constexpr int kScQBytes = kRowsPerGroup * kScValues;     // 4096
+constexpr int kScDBytes = kRowsPerGroup * kScBlocks * 2; // 256
+constexpr int kChunkBytes = 1024;                        // 2 blocks x 16 rows
+
+struct Shape {
+    int64_t N, K;
+    int64_t KB;   // blocks per row
+    int64_t G;    // row groups
+    int64_t NSC;  // super-chunks per row
+    int64_t Kp;   // K padded to a multiple of 256
+    int64_t stride;  // activation slot stride in bytes
+    int64_t q_bytes;  // packed q region
+    int64_t d_bytes;  // packed scale region
+};
+
+inline __host__ __device__ int64_t align_up(int64_t v, int64_t a) {
+    return (v + a - 1) / a * a;
+}
+
+inline Shape make_shape(int64_t N, int64_t K) {
+    Shape s;
+    s.N = N;
+    s.K = K;
+    s.KB = K / kBlock;
+    s.G = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    s.NSC = (s.KB + kScBlocks - 1) / kScBlocks;
+    s.Kp = s.NSC * kScValues;
+    s.stride = align_up(s.Kp + s.Kp / kBlock * 2, 256);
+    s.q_bytes = s.G * s.NSC * kScQBytes;
+    s.d_bytes = s.G * s.NSC * kScDBytes;
+    return s;
+}
+
+// k-slot of the MFMA operand -> starting byte inside the 32-value block
+__host__ __device__ constexpr int slot_pos(int slot) {
+    return 8 * (((slot & 1) << 1) | (slot >> 1));
+}
+// byte offset inside the block (multiple of 8) -> k-slot (inverse of slot_pos)
+__host__ __device__ constexpr int pos_slot(int pos8) {
+    return ((pos8 & 1) << 1) | (pos8 >> 1);
+}
+
+// ------------------------------------------------------------------------
+// q8_0 quantisation of one 8-value segment by a group of 4 lanes that
+// together hold a 32-value block.  Lanes of the group must be 4 consecutive
+// lanes starting at a multiple of 4 and all of them must be active.
+// ------------------------------------------------------------------------
+struct QuantSeg {
+    uint32_t lo, hi;  // 8 int8 values, little-endian
+    uint16_t d16;     // binary16 scale of the block
+};
+
+__device__ inline QuantSeg quantize_segment(const float v[8]) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+    // absmax of the 32-value block across the 4-lane group (max is exact)
+    a = fmaxf(a, __shfl_xor(a, 1, 4));
+    a = fmaxf(a, __shfl_xor(a, 2, 4));
+    QuantSeg r;
+    if (a == 0.0f) {
+        r.lo = r.hi = 0u;
+        r.d16 = 0;
+        return r;
+    }
+    const float d = a / 127.0f;  // correctly rounded (no fast-math)
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float q = roundf(v[i] / d);  // IEEE division, ties away from zero
+        q = fminf(fmaxf(q, -127.0f), 127.0f);
+        const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)q;
+        w[i >> 2] |= b << (8 * (i & 3));
+    }
+    r.lo = w[0];
+    r.hi = w[1];
+    r.d16 = __builtin_bit_cast(uint16_t, (_Float16)d);  // round to nearest even
+    return r;
+}
+
+// ------------------------------------------------------------------------
+// Kernel launchers (host).  Shapes and pointers are validated by the caller.
+// ------------------------------------------------------------------------
+hipError_t launch_pack_weights(const float* W, const Shape& s, uint8_t* Wq,
+                               hipStream_t st);
+hipError_t launch_pack_weights_q(const int8_t* q, const uint16_t* d16,
+                                 const Shape& s, uint8_t* Wq, hipStream_t st);
+hipError_t launch_unpack_weights(const uint8_t* Wq, const Shape& s, int8_t* q,
+                                 uint16_t* d16, hipStream_t st);
+hipError_t launch_quantize_acts(const float* X, int n_rows, const Shape& s,
+                                uint8_t* Xq, hipStream_t st);
+
+// Matmul tiling: chosen from (N, K) only, so that the fp32 summation order
+// of every output never depends on the live batch.
+struct Tiling {
+    int ks;  // waves splitting K inside a workgroup (K-slices)
+};
+Tiling choose_tiling(const Shape& s);
+
+enum class Engine { kMfma, kDot4 };
+hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
+                         const int32_t* batch_index, int n_live,
+                         const Shape& s, const Tiling& t, float* Y,
+                         hipStream_t st);
+
+}  // namespace q8

@@ -1,0 +1,148 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, reports layout sizes, and rejects invalid arguments before making
+any HIP call (so these tests need no GPU and launch nothing)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8narrow.h")
+
+
+@pytest.fixture(scope="module")
+def q8():
+    import quantized_weight_streaming_q8_amd as q8
+    return q8
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b(q8_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_abi():
+    names = header_functions()
+    for core in ("q8_pack_weights", "q8_quantize_acts", "q8_matmul_narrow"):
+        assert core in names
+    assert len(names) == 11, names
+
+
+def test_every_declared_symbol_is_exported(q8):
+    lib = ctypes.CDLL(q8.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert set(header_functions()) == set(q8._SIGNATURES)
+
+
+def test_constants_agree_with_header(q8):
+    text = open(HEADER).read()
+    assert int(re.search(r"#define Q8_MAX_SLOTS (\d+)", text).group(1)) == q8.Q8_MAX_SLOTS == 16
+    assert int(re.search(r"#define Q8_BLOCK (\d+)", text).group(1)) == q8.Q8_BLOCK == 32
+    for name in ("Q8_OK", "Q8_ERR_INVALID_ARG", "Q8_ERR_UNSUPPORTED", "Q8_ERR_HIP",
+                 "Q8_PATH_AUTO", "Q8_PATH_MFMA", "Q8_PATH_DOT4"):
+        val = int(re.search(name + r"\s*=\s*(\d+)", text).group(1))
+        assert getattr(q8, name) == val, name
+
+
+def test_status_strings(q8):
+    assert q8.status_str(0) == "Q8_OK"
+    assert q8.status_str(1) == "Q8_ERR_INVALID_ARG"
+    assert q8.status_str(2) == "Q8_ERR_UNSUPPORTED"
+    assert q8.status_str(3) == "Q8_ERR_HIP"
+    assert q8.status_str(99) == "Q8_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("N,K", [(768, 768), (7168, 5120), (5120, 17408),
+                                 (151936, 5120), (1, 32), (17, 288)])
+def test_layout_sizes(q8, N, K):
+    G = -(-N // 16)
+    NSC = -(-K // 256)
+    assert q8.q8_packed_weight_bytes(N, K) == G * NSC * (4096 + 256)
+    Kp = NSC * 256
+    stride = -(-(Kp + 2 * Kp // 32) // 256) * 256
+    assert q8.q8_act_slot_stride(K) == stride
+    assert stride % 256 == 0 and stride >= K + 2 * (K // 32)
+    assert q8.q8_act_buffer_bytes(K) == 16 * stride
+
+
+def test_packed_size_is_weight_bytes_plus_padding(q8):
+    # 34 bytes per 32 weights when N % 16 == 0 and K % 256 == 0
+    assert q8.q8_packed_weight_bytes(7168, 5120) == 7168 * 5120 * 34 // 32
+
+
+@pytest.mark.parametrize("N,K", [(0, 32), (-1, 32), (4, 0), (4, 31), (4, 48),
+                                 (4, 1 << 24), (1 << 30, 1 << 12)])
+def test_invalid_shapes_have_no_size(q8, N, K):
+    assert q8.q8_packed_weight_bytes(N, K) == 0
+
+
+def test_invalid_k_has_no_slot_stride(q8):
+    assert q8.q8_act_slot_stride(0) == 0
+    assert q8.q8_act_slot_stride(33) == 0
+    assert q8.q8_act_buffer_bytes(33) == 0
+
+
+# Fake but well-aligned addresses: every call below must be rejected by the
+# host-side checks before any pointer is used or any HIP call is made.
+P = 1 << 20
+
+
+def _rc(fn, *args):
+    return fn(*args)
+
+
+@pytest.mark.parametrize("args", [
+    (None, P, P, 4, 64, 64, P, None),       # Wq null
+    (P, None, P, 4, 64, 64, P, None),       # Xq null
+    (P, P, None, 4, 64, 64, P, None),       # batch_index null
+    (P, P, P, 4, 64, 64, None, None),       # Y null
+    (P, P, P, 0, 64, 64, P, None),          # n_live 0
+    (P, P, P, 17, 64, 64, P, None),         # n_live beyond the slots
+    (P, P, P, -3, 64, 64, P, None),
+    (P, P, P, 4, 0, 64, P, None),           # N = 0
+    (P, P, P, 4, 64, 48, P, None),          # K % 32 != 0
+    (P, P, P, 4, 64, 16, P, None),          # K < 32
+    (P + 8, P, P, 4, 64, 64, P, None),      # Wq misaligned
+    (P, P + 4, P, 4, 64, 64, P, None),      # Xq misaligned
+    (P, P, P + 2, 4, 64, 64, P, None),      # batch_index misaligned
+    (P, P, P, 4, 64, 64, P + 1, None),      # Y misaligned
+])
+def test_matmul_rejects_invalid_arguments(q8, args):
+    assert q8.library().q8_matmul_narrow(*args) == q8.Q8_ERR_INVALID_ARG
+
+
+def test_matmul_path_rejects_unknown_engine(q8):
+    lib = q8.library()
+    assert lib.q8_matmul_narrow_path(P, P, P, 4, 64, 64, P, None, 3) == q8.Q8_ERR_INVALID_ARG
+    assert lib.q8_matmul_narrow_path(P, P, P, 4, 64, 64, P, None, -1) == q8.Q8_ERR_INVALID_ARG
+
+
+def test_other_entry_points_reject_invalid_arguments(q8):
+    lib = q8.library()
+    bad = q8.Q8_ERR_INVALID_ARG
+    assert lib.q8_pack_weights(None, 4, 64, P, None) == bad
+    assert lib.q8_pack_weights(P, 4, 64, None, None) == bad
+    assert lib.q8_pack_weights(P + 4, 4, 64, P, None) == bad
+    assert lib.q8_pack_weights(P, 4, 40, P, None) == bad
+    assert lib.q8_pack_weights_q(P, P, 4, 64, P + 8, None) == bad
+    assert lib.q8_pack_weights_q(P + 4, P, 4, 64, P, None) == bad
+    assert lib.q8_pack_weights_q(P, P + 1, 4, 64, P, None) == bad
+    assert lib.q8_unpack_weights(P, 0, 64, P, P, None) == bad
+    assert lib.q8_unpack_weights(None, 4, 64, P, P, None) == bad
+    assert lib.q8_quantize_acts(P, 0, 64, P, None) == bad
+    assert lib.q8_quantize_acts(P, 17, 64, P, None) == bad
+    assert lib.q8_quantize_acts(P, 4, 65, P, None) == bad
+    assert lib.q8_quantize_acts(P + 4, 4, 64, P, None) == bad
+    assert lib.q8_quantize_acts(P, 4, 64, None, None) == bad
+
+
+def test_binding_raises_on_rejected_call(q8):
+    with pytest.raises(q8.Q8Error) as e:
+        q8.q8_matmul_narrow(P, P, P, 0, 64, 64, P, stream=0)
+    assert e.value.status == q8.Q8_ERR_INVALID_ARG
+    assert "Q8_ERR_INVALID_ARG" in str(e.value)

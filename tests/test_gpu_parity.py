@@ -1,0 +1,324 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Bars: quantised int8 blocks and binary16 scales bit-exact; per-block int32
+sums exact; fp32 outputs within 1e-4 * sum|block terms| + 1e-6 of the
+oracle's double sum; per-token columns bit-identical to single-token calls;
+the MFMA and DOT4 engines bit-identical to each other.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import (gpu_matmul, gpu_pack, gpu_pack_q, gpu_quantize_acts,
+                      gpu_unpack, sample_rows, slots_host, to_dev, within_tau,
+                      write_slots)
+
+pytestmark = pytest.mark.gpu
+
+MFMA, DOT4 = 1, 2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import quantized_weight_streaming_q8_amd as q8
+    assert q8.q8_device_supported(), "device is not gfx950"
+    yield
+    torch.cuda.synchronize()
+
+
+def _ragged_x(K, seed, outliers=False):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((16, K), dtype=np.float32)
+    if outliers:
+        X[:, rng.choice(K, max(1, K // 100), replace=False)] *= np.float32(20)
+    X[3, :64] = 0.0            # zero blocks
+    X[5] *= np.float32(1e-5)   # binary16-subnormal scales
+    return X
+
+
+# ---------------------------------------------------------------- quantiser
+
+@pytest.mark.parametrize("K", [32, 288, 768, 3072, 4128, 5120, 7168, 17408, 18432])
+def test_quantize_acts_bit_exact(K):
+    X = _ragged_x(K, seed=K, outliers=True)
+    Xq = gpu_quantize_acts(X)
+    q, d = slots_host(Xq, K)
+    qo, do = oracle.quantize_rows(X)
+    assert np.array_equal(q, qo)
+    assert np.array_equal(d, do)
+    # padding of each slot is written as zero
+    raw = Xq.view(16, -1).cpu().numpy()
+    Kp = (K + 255) // 256 * 256
+    assert not raw[:, K:Kp].any()
+    assert not raw[:, Kp + 2 * (K // 32):Kp + Kp // 16].any()
+
+
+def test_quantize_acts_partial_rows_leave_other_slots():
+    K = 1024
+    import quantized_weight_streaming_q8_amd as q8
+    Xq = q8.empty_act_slots(K)
+    Xq.fill_(0x5A)
+    X = _ragged_x(K, seed=1)[:5]
+    gpu_quantize_acts(X, Xq)
+    raw = Xq.view(16, -1).cpu().numpy()
+    assert np.all(raw[5:] == 0x5A)
+    q, d = slots_host(Xq, K)
+    qo, do = oracle.quantize_rows(X)
+    assert np.array_equal(q[:5], qo) and np.array_equal(d[:5], do)
+
+
+# ------------------------------------------------------------------- packer
+
+@pytest.mark.parametrize("N,K", [(1, 32), (17, 288), (100, 800), (768, 768),
+                                 (2304, 768), (768, 3072), (33, 4128)])
+def test_pack_weights_bit_exact_small(N, K):
+    rng = np.random.default_rng(N * 7 + K)
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    W[0, :32] = 0.0
+    Wq = gpu_pack(W)
+    q, d = gpu_unpack(Wq, N, K)
+    qo, do = oracle.quantize_rows(W)
+    assert np.array_equal(q, qo) and np.array_equal(d, do)
+
+
+@pytest.mark.parametrize("key,idx", [("qwen3_layer", 0), ("qwen3_layer", 1),
+                                     ("qwen3_layer", 2), ("qwen3_layer", 3),
+                                     ("large_dense", 1)])
+def test_pack_weights_bit_exact_full(key, idx):
+    w = wl.WORKLOADS[key]
+    m = w.matrices[idx]
+    W = wl.weights(w.config, idx, m.N, m.K)
+    Wq = gpu_pack(W)
+    q, d = gpu_unpack(Wq, m.N, m.K)
+    qo, do = oracle.quantize_rows(W)
+    assert np.array_equal(q, qo) and np.array_equal(d, do)
+
+
+def test_pack_q_round_trip_any_int8():
+    rng = np.random.default_rng(5)
+    N, K = 37, 1056
+    q = rng.integers(-128, 128, size=(N, K)).astype(np.int8)
+    d = rng.integers(0, 0x7c00, size=(N, K // 32)).astype(np.uint16)
+    Wq = gpu_pack_q(q, d)
+    q2, d2 = gpu_unpack(Wq, N, K)
+    assert np.array_equal(q, q2) and np.array_equal(d, d2)
+
+
+# ------------------------------------------------------------------- matmul
+
+def _oracle_y(W, X, bi, rows=None):
+    Wr = W if rows is None else W[rows]
+    qw, dw = oracle.quantize_rows(Wr)
+    qx, dx = oracle.quantize_rows(X)
+    return oracle.matmul(qw, dw, qx, dx, bi)
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (17, 288), (15, 2080), (100, 800),
+                                 (16, 256), (33, 4128), (768, 768), (40, 17408)])
+def test_matmul_ragged_shapes(N, K):
+    rng = np.random.default_rng(N + K)
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    X = _ragged_x(K, seed=K + 1)
+    Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
+    for bi in (np.array([0]), np.array([3, 3, 9]), rng.permutation(16),
+               np.array([15, 2, 2, 7, 0, 11, 5])):
+        bi = bi.astype(np.int32)
+        Yo, Ao = _oracle_y(W, X, bi)
+        Ym = gpu_matmul(Wq, Xq, bi, N, K, MFMA)
+        ok, worst = within_tau(Ym, Yo, Ao)
+        assert ok, (N, K, bi, worst)
+        Yd = gpu_matmul(Wq, Xq, bi, N, K, DOT4)
+        assert np.array_equal(Ym.view(np.uint32), Yd.view(np.uint32)), (N, K, bi)
+
+
+@pytest.mark.parametrize("n_live", [1, 2, 4])
+def test_single_768(n_live):
+    w = wl.WORKLOADS["single"]
+    W, X = wl.workload_inputs("single", 0)
+    bi = wl.batch_index(w.config, n_live, random=False)
+    Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
+    Yo, Ao = _oracle_y(W, X, bi)
+    for path in (0, MFMA, DOT4):
+        ok, worst = within_tau(gpu_matmul(Wq, Xq, bi, 768, 768, path), Yo, Ao)
+        assert ok, (path, worst)
+
+
+def test_llama68m_stack():
+    w = wl.WORKLOADS["llama68m"]
+    for idx, m in enumerate(w.matrices):
+        W, X = wl.workload_inputs("llama68m", idx)
+        Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
+        for n_live in w.n_live:
+            bi = wl.batch_index(w.config, n_live, random=False)
+            Yo, Ao = _oracle_y(W, X, bi)
+            Y = gpu_matmul(Wq, Xq, bi, m.N, m.K)
+            ok, worst = within_tau(Y, Yo, Ao)
+            assert ok, (m.name, n_live, worst)
+
+
+def test_block_sums_exact_through_the_kernel():
+    """With weight scale 1 on block b0 and +0 elsewhere, and activation scale
+    1, Y[t,n] is exactly the int32 block sum S_b0 (every other term is +0 and
+    S < 2^24 is exact in fp32)."""
+    rng = np.random.default_rng(19)
+    N, K = 48, 2080  # 65 blocks: a partial last super-chunk
+    KB = K // 32
+    qw = rng.integers(-128, 128, size=(N, K)).astype(np.int8)
+    qx = rng.integers(-128, 128, size=(16, K)).astype(np.int8)
+    qw[0, :] = -128
+    qx[4, :] = -128  # S = 2^19 for row 0, slot 4
+    import quantized_weight_streaming_q8_amd as q8
+    Xq = q8.empty_act_slots(K)
+    write_slots(Xq, K, qx, np.full((16, KB), 0x3c00, dtype=np.uint16))
+    bi = np.array([4, 0, 15, 7, 4], dtype=np.int32)
+    S = oracle.block_dots(qw, qx, bi)
+    for b0 in (0, 1, 7, 8, 31, 63, 64):
+        d = np.zeros((N, KB), dtype=np.uint16)
+        d[:, b0] = 0x3c00
+        Wq = gpu_pack_q(qw, d)
+        for path in (MFMA, DOT4):
+            Y = gpu_matmul(Wq, Xq, bi, N, K, path)
+            assert np.array_equal(Y, S[:, :, b0].astype(np.float32)), (b0, path)
+    assert S[0, 0, 0] == 1 << 19
+
+
+def test_pad_slots_do_not_leak():
+    """Slots that are not live may hold anything (here random bytes and
+    infinite / NaN scales): the live outputs do not change by a bit."""
+    rng = np.random.default_rng(23)
+    N, K = 64, 1024
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    X = rng.standard_normal((16, K), dtype=np.float32)
+    Wq = gpu_pack(W)
+    Xq = gpu_quantize_acts(X)
+    bi = np.array([2, 9, 5], dtype=np.int32)
+    clean = {p: gpu_matmul(Wq, Xq, bi, N, K, p) for p in (MFMA, DOT4)}
+    raw = Xq.view(16, -1)
+    for s in range(16):
+        if s in bi:
+            continue
+        raw[s].copy_(torch.from_numpy(rng.integers(0, 256, raw.shape[1], dtype=np.uint8)))
+    import quantized_weight_streaming_q8_amd as q8
+    qv, dv = q8.split_act_slots(Xq, K)
+    dv[0].fill_(0x7c00)   # +inf
+    dv[1].fill_(0x7e00)   # NaN
+    for p in (MFMA, DOT4):
+        assert np.array_equal(gpu_matmul(Wq, Xq, bi, N, K, p).view(np.uint32),
+                              clean[p].view(np.uint32))
+
+
+def test_bad_batch_index_gives_nan_row():
+    rng = np.random.default_rng(29)
+    N, K = 40, 512
+    W = rng.standard_normal((N, K), dtype=np.float32)
+    X = rng.standard_normal((16, K), dtype=np.float32)
+    Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
+    bi = np.array([1, 16, -1, 3, 1 << 30], dtype=np.int32)
+    Yo, Ao = _oracle_y(W, X, np.array([1, 3], dtype=np.int32))
+    for p in (MFMA, DOT4):
+        Y = gpu_matmul(Wq, Xq, bi, N, K, p)
+        assert np.all(np.isnan(Y[[1, 2, 4]]))
+        assert within_tau(Y[[0, 3]], Yo, Ao)[0]
+
+
+def test_columns_equal_single_token_calls():
+    """Row t of a batched call is bit-identical to the call with n_live = 1
+    and batch_index = {batch_index[t]}, for every t, on both engines."""
+    N, K = 2304, 5120
+    rng = np.random.default_rng(31)
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    X = _ragged_x(K, seed=3, outliers=True)
+    Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
+    bi = rng.permutation(16).astype(np.int32)
+    for p in (MFMA, DOT4):
+        Y = gpu_matmul(Wq, Xq, bi, N, K, p)
+        for t in range(16):
+            y1 = gpu_matmul(Wq, Xq, bi[t:t + 1], N, K, p)
+            assert np.array_equal(Y[t].view(np.uint32), y1[0].view(np.uint32)), (p, t)
+        for n in (3, 8, 13):
+            Yn = gpu_matmul(Wq, Xq, bi[:n], N, K, p)
+            assert np.array_equal(Yn.view(np.uint32), Y[:n].view(np.uint32)), (p, n)
+
+
+# -------------------------------------------- full-size model-shaped layers
+
+def test_qwen3_layer_every_live_batch():
+    """Qwen3-14B decode layer, every live batch 1..16 with a seeded random
+    batch_index, in the launch configuration the benchmark times; sampled
+    rows against the oracle, and the two engines bit-identical on all rows."""
+    w = wl.WORKLOADS["qwen3_layer"]
+    for idx, m in enumerate(w.matrices):
+        W, X = wl.workload_inputs("qwen3_layer", idx)
+        Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
+        rows = sample_rows(m.N, 96, seed=idx)
+        qw, dw = oracle.quantize_rows(W[rows])
+        qx, dx = oracle.quantize_rows(X)
+        del W
+        for n_live in w.n_live:
+            bi = wl.batch_index(w.config, n_live, random=True)
+            Y = gpu_matmul(Wq, Xq, bi, m.N, m.K)
+            Yo, Ao = oracle.matmul(qw, dw, qx, dx, bi)
+            ok, worst = within_tau(Y[:, rows], Yo, Ao)
+            assert ok, (m.name, n_live, worst)
+            if n_live in (1, 7, 16):
+                Yd = gpu_matmul(Wq, Xq, bi, m.N, m.K, DOT4)
+                assert np.array_equal(Y.view(np.uint32), Yd.view(np.uint32)), (m.name, n_live)
+        del Wq
+        torch.cuda.empty_cache()
+
+
+def test_qwen3_head_columns():
+    w = wl.WORKLOADS["qwen3_head"]
+    m = w.matrices[0]
+    W, X = wl.workload_inputs("qwen3_head", 0)
+    Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
+    rows = sample_rows(m.N, 128, seed=4)
+    qw, dw = oracle.quantize_rows(W[rows])
+    del W
+    qx, dx = oracle.quantize_rows(X)
+    Y16 = None
+    for n_live in w.n_live:
+        bi = wl.batch_index(w.config, n_live, random=False)
+        Y = gpu_matmul(Wq, Xq, bi, m.N, m.K)
+        Yo, Ao = oracle.matmul(qw, dw, qx, dx, bi)
+        ok, worst = within_tau(Y[:, rows], Yo, Ao)
+        assert ok, (n_live, worst)
+        if n_live == 16:
+            Y16 = Y
+    for t in range(16):
+        y1 = gpu_matmul(Wq, Xq, np.array([t], dtype=np.int32), m.N, m.K)
+        assert np.array_equal(y1[0].view(np.uint32), Y16[t].view(np.uint32)), t
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_large_dense_schedule(idx):
+    """A 1000-step decode schedule with n_live uniform on 1..16: every step's
+    rows are the 16-slot result's rows gathered by batch_index, bit for bit;
+    the 16-slot result matches the oracle on sampled rows."""
+    w = wl.WORKLOADS["large_dense"]
+    m = w.matrices[idx]
+    W, X = wl.workload_inputs("large_dense", idx)
+    Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
+    rows = sample_rows(m.N, 96, seed=5 + idx)
+    ident = np.arange(16, dtype=np.int32)
+    Yo, Ao = _oracle_y(W, X, ident, rows)
+    del W
+    Y16 = gpu_matmul(Wq, Xq, ident, m.N, m.K)
+    ok, worst = within_tau(Y16[:, rows], Yo, Ao)
+    assert ok, worst
+    import quantized_weight_streaming_q8_amd as q8
+    sched = wl.schedule(w.config, steps=1000)
+    Y = torch.empty((16, m.N), dtype=torch.float32, device="cuda")
+    ref = torch.from_numpy(Y16).cuda()
+    bad = torch.zeros((), dtype=torch.int64, device="cuda")
+    for bi in sched:
+        bi_d = to_dev(bi)
+        n = bi.size
+        q8.q8_matmul_narrow(Wq, Xq, bi_d, n, m.N, m.K, Y)
+        bad += (Y[:n].view(torch.int32) != ref[bi_d.long()].view(torch.int32)).sum()
+    assert int(bad) == 0
