@@ -75,16 +75,13 @@ typedef enum q8_path {
  * the matmul kernels); use q8_unpack_weights to read it back. */
 size_t q8_packed_weight_bytes(int64_t N, int64_t K);
 
-/* Bytes between consecutive activation slots for K inputs; 0 if invalid.
+/* Bytes of an activation slot buffer for K inputs; 0 if K is invalid.
  *
- * Activation slot buffer layout (public): Q8_MAX_SLOTS slots; slot s starts
- * at byte s * stride and holds int8 q[Kp] followed by binary16 d[Kp/32],
- * where Kp is K rounded up to a multiple of 256.  Entries at and beyond K
- * (resp. K/32) are padding: q8_quantize_acts writes them as zero and the
- * matmul never uses them.  stride is a multiple of 256 bytes. */
-size_t q8_act_slot_stride(int64_t K);
-
-/* Bytes of a whole activation slot buffer: Q8_MAX_SLOTS * stride. */
+ * The slot buffer holds Q8_MAX_SLOTS quantised activation rows (slots).  Its
+ * layout is the packed layout of a Q8_MAX_SLOTS x K weight matrix whose row s
+ * is slot s: q8_quantize_acts fills it from fp32 rows, and q8_pack_weights_q /
+ * q8_unpack_weights with N = Q8_MAX_SLOTS write or read all slots in
+ * canonical q8_0 form.  Equal to q8_packed_weight_bytes(Q8_MAX_SLOTS, K). */
 size_t q8_act_buffer_bytes(int64_t K);
 
 /* -------------------------------------------------------------- packing */
@@ -124,9 +121,11 @@ q8_status q8_quantize_acts(const float* X, int n_rows, int64_t K, void* Xq,
  * order.  1 <= n_live <= Q8_MAX_SLOTS.
  *
  * Each weight block is read from memory once per call and used for every
- * live token.  The fp32 summation order depends only on (N, K), never on
- * n_live or on the other tokens, so row t of Y is bit-identical to a call
- * with n_live = 1 and batch_index = {batch_index[t]}.
+ * live token.  The fp32 summation order (a fixed tree over K: blocks in
+ * order within a slice, slices in order within a split, splits in order)
+ * depends only on (N, K), never on n_live or on the other tokens, so row t
+ * of Y is bit-identical to a call with n_live = 1 and batch_index =
+ * {batch_index[t]}.
  *
  * A batch_index entry outside [0, 16) cannot be checked on the host without
  * a synchronisation; it is not read through: that token's row of Y is set
@@ -141,6 +140,31 @@ q8_status q8_matmul_narrow_path(const void* Wq, const void* Xq,
                                 const int32_t* batch_index, int n_live,
                                 int64_t N, int64_t K, float* Y,
                                 hipStream_t stream, q8_path path);
+
+/* ---------------------------------------------- workspace execution */
+
+/* Bytes of workspace q8_matmul_narrow_ws needs for an N x K matrix; 0 when
+ * the shape is not split across workgroups (then no workspace is needed) or
+ * the shape is invalid. */
+size_t q8_matmul_workspace_bytes(int64_t N, int64_t K);
+
+/* q8_matmul_narrow, executed with the K splits of every row block spread
+ * over separate workgroups, which balances small-N shapes over the whole GPU.
+ * The splits meet through `workspace` (device memory, 256-byte aligned, at
+ * least q8_matmul_workspace_bytes(N, K) bytes): each split publishes its
+ * partial sums, and the last to arrive adds them in split order.  The result
+ * is bit-identical to q8_matmul_narrow on the same arguments.
+ *
+ * The workspace must be zero-filled before its first use; every completed
+ * call leaves it ready for the next one.  A workspace must not be shared by
+ * calls that can run at the same time (calls on one stream are fine).
+ * workspace may be NULL when q8_matmul_workspace_bytes(N, K) is 0.  A
+ * workspace that is missing, misaligned or too small is an invalid
+ * argument. */
+q8_status q8_matmul_narrow_ws(const void* Wq, const void* Xq,
+                              const int32_t* batch_index, int n_live,
+                              int64_t N, int64_t K, float* Y, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------- misc */
 

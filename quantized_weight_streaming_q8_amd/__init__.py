@@ -35,7 +35,6 @@ Q8_PATH_DOT4 = 2
 _vp, _i64, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 _SIGNATURES = {
     "q8_packed_weight_bytes": ([_i64, _i64], ctypes.c_size_t),
-    "q8_act_slot_stride": ([_i64], ctypes.c_size_t),
     "q8_act_buffer_bytes": ([_i64], ctypes.c_size_t),
     "q8_pack_weights": ([_vp, _i64, _i64, _vp, _vp], _i32),
     "q8_pack_weights_q": ([_vp, _vp, _i64, _i64, _vp, _vp], _i32),
@@ -43,6 +42,8 @@ _SIGNATURES = {
     "q8_quantize_acts": ([_vp, _i32, _i64, _vp, _vp], _i32),
     "q8_matmul_narrow": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp], _i32),
     "q8_matmul_narrow_path": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp, _i32], _i32),
+    "q8_matmul_workspace_bytes": ([_i64, _i64], ctypes.c_size_t),
+    "q8_matmul_narrow_ws": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp], _i32),
     "q8_device_supported": ([], _i32),
     "q8_status_str": ([_i32], ctypes.c_char_p),
 }
@@ -114,10 +115,6 @@ def q8_packed_weight_bytes(N: int, K: int) -> int:
     return int(_lib.q8_packed_weight_bytes(N, K))
 
 
-def q8_act_slot_stride(K: int) -> int:
-    return int(_lib.q8_act_slot_stride(K))
-
-
 def q8_act_buffer_bytes(K: int) -> int:
     return int(_lib.q8_act_buffer_bytes(K))
 
@@ -156,6 +153,20 @@ def q8_matmul_narrow_path(Wq, Xq, batch_index, n_live: int, N: int, K: int, Y,
            "q8_matmul_narrow_path")
 
 
+def q8_matmul_workspace_bytes(N: int, K: int) -> int:
+    return int(_lib.q8_matmul_workspace_bytes(N, K))
+
+
+def q8_matmul_narrow_ws(Wq, Xq, batch_index, n_live: int, N: int, K: int, Y,
+                        workspace, workspace_bytes: int | None = None,
+                        stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.q8_matmul_narrow_ws(_ptr(Wq), _ptr(Xq), _ptr(batch_index), n_live, N, K,
+                                    _ptr(Y), _ptr(workspace), workspace_bytes, _stream(stream)),
+           "q8_matmul_narrow_ws")
+
+
 def q8_device_supported() -> bool:
     return bool(_lib.q8_device_supported())
 
@@ -169,6 +180,15 @@ def empty_packed_weights(N: int, K: int, device="cuda") -> torch.Tensor:
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
+def zeroed_workspace(N: int, K: int, device="cuda") -> torch.Tensor | None:
+    """A zero-filled workspace for q8_matmul_narrow_ws (None if the shape
+    needs none)."""
+    nbytes = q8_matmul_workspace_bytes(N, K)
+    if nbytes == 0:
+        return None
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
 def empty_act_slots(K: int, device="cuda") -> torch.Tensor:
     nbytes = q8_act_buffer_bytes(K)
     if nbytes == 0:
@@ -176,12 +196,17 @@ def empty_act_slots(K: int, device="cuda") -> torch.Tensor:
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
-def split_act_slots(Xq: torch.Tensor, K: int):
-    """Views (q int8 [16][K], d16 int16 [16][K/32]) of a slot buffer, from the
-    public slot layout (slot s at s*stride: int8 q[Kp], binary16 d[Kp/32])."""
-    stride = q8_act_slot_stride(K)
-    kp = (K + 255) // 256 * 256
-    slots = Xq.view(Q8_MAX_SLOTS, stride)
-    q = slots[:, :K].view(torch.int8)
-    d = slots[:, kp:kp + 2 * (K // Q8_BLOCK)].view(torch.int16)
+def read_act_slots(Xq: torch.Tensor, K: int, stream=None):
+    """All slots of a slot buffer in canonical q8_0 form:
+    (q int8 [16][K], d16 int16 [16][K/32]) device tensors."""
+    q = torch.empty((Q8_MAX_SLOTS, K), dtype=torch.int8, device=Xq.device)
+    d = torch.empty((Q8_MAX_SLOTS, K // Q8_BLOCK), dtype=torch.int16, device=Xq.device)
+    q8_unpack_weights(Xq, Q8_MAX_SLOTS, K, q, d, stream)
     return q, d
+
+
+def write_act_slots(Xq: torch.Tensor, K: int, q: torch.Tensor, d16: torch.Tensor,
+                    stream=None) -> None:
+    """Write all 16 slots from canonical q8_0 (q int8 [16][K], d16 int16
+    [16][K/32] binary16 bits)."""
+    q8_pack_weights_q(q, d16, Q8_MAX_SLOTS, K, Xq, stream)

@@ -60,13 +60,8 @@ size_t q8_packed_weight_bytes(int64_t N, int64_t K) {
     return (size_t)(s.q_bytes + s.d_bytes);
 }
 
-size_t q8_act_slot_stride(int64_t K) {
-    if (!valid_shape(1, K)) return 0;
-    return (size_t)q8::make_shape(1, K).stride;
-}
-
 size_t q8_act_buffer_bytes(int64_t K) {
-    return (size_t)Q8_MAX_SLOTS * q8_act_slot_stride(K);
+    return q8_packed_weight_bytes(Q8_MAX_SLOTS, K);
 }
 
 q8_status q8_pack_weights(const float* W, int64_t N, int64_t K, void* Wq,
@@ -120,7 +115,7 @@ q8_status q8_matmul_narrow_path(const void* Wq, const void* Xq,
     const q8::Engine e = path == Q8_PATH_DOT4 ? q8::Engine::kDot4 : q8::Engine::kMfma;
     return from_hip(q8::launch_matmul(e, static_cast<const uint8_t*>(Wq),
                                       static_cast<const uint8_t*>(Xq), batch_index,
-                                      n_live, s, t, Y, stream));
+                                      n_live, s, t, Y, nullptr, stream));
 }
 
 q8_status q8_matmul_narrow(const void* Wq, const void* Xq,
@@ -128,6 +123,29 @@ q8_status q8_matmul_narrow(const void* Wq, const void* Xq,
                            int64_t K, float* Y, hipStream_t stream) {
     return q8_matmul_narrow_path(Wq, Xq, batch_index, n_live, N, K, Y, stream,
                                  Q8_PATH_AUTO);
+}
+
+size_t q8_matmul_workspace_bytes(int64_t N, int64_t K) {
+    if (!valid_shape(N, K)) return 0;
+    const q8::Shape s = q8::make_shape(N, K);
+    return q8::workspace_bytes(s, q8::choose_tiling(s));
+}
+
+q8_status q8_matmul_narrow_ws(const void* Wq, const void* Xq,
+                              const int32_t* batch_index, int n_live, int64_t N,
+                              int64_t K, float* Y, void* workspace,
+                              size_t workspace_size, hipStream_t stream) {
+    if (!valid_shape(N, K) || n_live < 1 || n_live > Q8_MAX_SLOTS || !aligned(Wq, 16) ||
+        !aligned(Xq, 16) || !aligned(batch_index, 4) || !aligned(Y, 4))
+        return Q8_ERR_INVALID_ARG;
+    const q8::Shape s = q8::make_shape(N, K);
+    const q8::Tiling t = q8::choose_tiling(s);
+    const size_t need = q8::workspace_bytes(s, t);
+    if (need > 0 && (!aligned(workspace, 256) || workspace_size < need)) return Q8_ERR_INVALID_ARG;
+    if (!current_device_ok()) return Q8_ERR_UNSUPPORTED;
+    return from_hip(q8::launch_matmul(q8::Engine::kMfma, static_cast<const uint8_t*>(Wq),
+                                      static_cast<const uint8_t*>(Xq), batch_index, n_live,
+                                      s, t, Y, need > 0 ? workspace : nullptr, stream));
 }
 
 int q8_device_supported(void) { return current_device_ok(); }

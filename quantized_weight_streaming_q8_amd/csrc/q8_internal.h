@@ -12,18 +12,19 @@
 //     with P = {0, 16, 8, 24}.  One 16-byte load per lane of a wave64 then
 //     holds this lane's 8-byte B operand of the MFMA for block 2c (h = 0) and
 //     block 2c+1 (h = 1): row = lane & 15, k-slot = lane >> 4.
-//   scale region, after the q region, 256 bytes per (group, super-chunk):
-//     half ((g*NSC + sc)*16 + j)*8 + bb = d[row 16g + j][block 8sc + bb]
+//   scale region, after the q region, 64 bytes per (group, chunk):
+//     half ((g*4*NSC + c)*16 + j)*2 + h = d[row 16g + j][block 2c + h]
+//     (c = chunk index along the row).  Four consecutive rows' scales of a
+//     chunk are 16 contiguous bytes, the operand of one lane of the MFMA
+//     output (rows 4*(lane >> 4) .. +3).
 //
-// The permutation P follows from how the activation operand is built: lane
-// (token t, k-slot s) loads 16 contiguous bytes of token t's canonical slot at
-// 64c + 16s (s = 0,1 hold block 2c, s = 2,3 block 2c+1) and one
-// v_permlane32_swap exchanges 8 bytes between lanes l and l+32, after which
-// lane slot s holds bytes P(s)..P(s)+7 of both blocks.  Any permutation is
-// exact here, since a block's 32 products are summed in integers.
-//
-// Activation slot buffer (public, see q8narrow.h): slot s at s*stride holds
-// int8 q[Kp] then binary16 d[Kp/32], Kp = 256*NSC.
+// The same layout holds the activation slot buffer: it is the packed form of a
+// 16 x K matrix whose row s is slot s.  A lane (token t = lane & 15, k-slot
+// g = lane >> 4) of the MFMA engine then finds its 8-byte A operand for blocks
+// 2c and 2c+1 in one 16-byte load at chunk offset (g*16 + slot)*16, and a
+// wave's activation load for one chunk of all 16 slots is 1 KB contiguous.
+// P is the k-slot -> byte-in-block map both operands share; any permutation
+// is exact, since a block's 32 products are summed in integers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,6 +39,7 @@ constexpr int kScBlocks = 8;      // blocks per super-chunk
 constexpr int kScValues = kScBlocks * kBlock;            // 256
 constexpr int kScQBytes = kRowsPerGroup * kScValues;     // 4096
 constexpr int kScDBytes = kRowsPerGroup * kScBlocks * 2; // 256
+constexpr int kChunkDBytes = kRowsPerGroup * 2 * 2;       // 64
 constexpr int kChunkBytes = 1024;                        // 2 blocks x 16 rows
 
 struct Shape {
@@ -46,9 +48,9 @@ struct Shape {
     int64_t G;    // row groups
     int64_t NSC;  // super-chunks per row
     int64_t Kp;   // K padded to a multiple of 256
-    int64_t stride;  // activation slot stride in bytes
     int64_t q_bytes;  // packed q region
     int64_t d_bytes;  // packed scale region
+    int64_t act_q_bytes;  // activation buffer: q region (16 rows)
 };
 
 inline __host__ __device__ int64_t align_up(int64_t v, int64_t a) {
@@ -63,9 +65,9 @@ inline Shape make_shape(int64_t N, int64_t K) {
     s.G = (N + kRowsPerGroup - 1) / kRowsPerGroup;
     s.NSC = (s.KB + kScBlocks - 1) / kScBlocks;
     s.Kp = s.NSC * kScValues;
-    s.stride = align_up(s.Kp + s.Kp / kBlock * 2, 256);
     s.q_bytes = s.G * s.NSC * kScQBytes;
     s.d_bytes = s.G * s.NSC * kScDBytes;
+    s.act_q_bytes = s.NSC * kScQBytes;
     return s;
 }
 
@@ -131,14 +133,21 @@ hipError_t launch_quantize_acts(const float* X, int n_rows, const Shape& s,
 // Matmul tiling: chosen from (N, K) only, so that the fp32 summation order
 // of every output never depends on the live batch.
 struct Tiling {
-    int ks;  // waves splitting K inside a workgroup (K-slices)
+    int rg;           // row groups of 16 rows per wave (MFMA engine)
+    int splits;       // K splits (level 2 of the summation tree)
+    int kw;           // wave slices per split (level 1)
+    bool nt_weights;  // non-temporal loads for the weight stream
 };
 Tiling choose_tiling(const Shape& s);
+// Workspace a split execution needs (0: the shape is not split).
+size_t workspace_bytes(const Shape& s, const Tiling& t);
 
 enum class Engine { kMfma, kDot4 };
+// workspace: nullptr for the single-workgroup evaluation of the tree, or a
+// zero-initialised buffer of workspace_bytes() for the split execution.
 hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
                          const int32_t* batch_index, int n_live,
                          const Shape& s, const Tiling& t, float* Y,
-                         hipStream_t st);
+                         void* workspace, hipStream_t st);
 
 }  // namespace q8

@@ -9,53 +9,86 @@
 //   y[t,n]  += float(S) * (float(dw[n,b]) * float(dx[slot_t,b]))
 //
 // with one fused multiply-add per term; dw*dx is exact in fp32 (two 11-bit
-// significands).  Each wave owns a contiguous K-slice (a run of 256-value
-// super-chunks) and accumulates its terms in ascending block order; the
-// KS waves of a workgroup then add their partial sums in wave order through
-// LDS.  KS and the slices depend only on (N, K), so the arithmetic of an
-// output never depends on n_live or on other tokens.
+// significands).  The fp32 summation follows one tree per (N, K), whatever
+// the live batch or execution strategy:
+//   * K is cut into S splits (contiguous runs of 256-value super-chunks),
+//     each split into KW wave slices;
+//   * a wave adds its terms in ascending block order;
+//   * level 1: a split's partial is the sum of its KW wave partials in order;
+//   * level 2: the output is the sum of the S split partials in order.
+// The plain entry point evaluates the whole tree in one workgroup of S*KW
+// waves (levels 1 and 2 through LDS).  The workspace entry point runs the S
+// splits of a row block as S workgroups: each evaluates level 1 and writes
+// its partial to the workspace; the last of them to arrive (a counter per
+// row block) evaluates level 2 and writes Y.  Both give the same bits, and
+// so does the DOT4 engine below, so a token's output never depends on
+// n_live, on the other tokens or on the entry point.
 //
 // Two int8 dot engines compute S, with the same accumulation order, so their
 // results are bit-identical:
 //   * MFMA: one v_mfma_i32_16x16x32_i8 per (16 rows, block) dots the block
-//     against 16 token slots at once.  A = activations (token = lane & 15),
-//     B = weights (row = lane & 15), D[token][row] -> lane holds row
-//     lane & 15 for tokens 4*(lane >> 4) + r.  The cost is the same for any
-//     n_live, so the weight stream is the only thing that scales.
+//     against 16 token slots at once.  A = weights (row = lane & 15), B =
+//     activations (token = lane & 15), D[row][token] -> lane holds token
+//     lane & 15 for rows 4*(lane >> 4) + r, so a lane needs one token's
+//     activation scales and four consecutive rows' weight scales, each one
+//     small load per chunk.  The cost is the same for any n_live: the weight
+//     stream is what the kernel spends its time on.  A wave covers RG row
+//     groups, so each activation load feeds 16*RG rows.
 //   * DOT4: one output row per lane, v_dot4 over the row's 32 bytes against
 //     the token's block (wave-uniform, so it comes through scalar loads).  Its
 //     VALU work grows with n_live.
 //
-// Token slots come from batch_index through the activation slot buffer (the
-// batch_index gather of "[feature] Enable Dynamic Batching", section
-// "Objective").  Lanes of tokens t >= n_live read token 0's slot and their
-// results are dropped; a slot index outside [0,16) is never read through
-// (slot 0 is read instead) and its output row is written as NaN.
+// Token slots come from batch_index ("[feature] Enable Dynamic Batching",
+// section "Objective": batch_index selects rows of a fixed, fully sized
+// buffer).  The slot buffer has the packed layout of a 16-row matrix, so the
+// activation operand of one chunk for all 16 slots is 1 KB contiguous.  Lanes
+// of tokens t >= n_live read token 0's slot and their results are dropped; a
+// slot index outside [0,16) is never read through (slot 0 is read instead)
+// and its output row is written as NaN.
 
 #include "q8_internal.h"
 
 #include <math.h>
 
+#include <algorithm>
+#ifdef Q8_TUNING
+#include <cstdlib>
+#endif
+
 namespace q8 {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMaxKs = 16;  // waves per workgroup at most (1024 threads)
+constexpr int kMaxKs = 16;             // waves per workgroup at most
+#ifndef Q8_RING
+#define Q8_RING 4
+#endif
+constexpr int kRing = Q8_RING;         // chunks in flight per wave (MFMA engine)
+constexpr size_t kMaxLds = 64 * 1024;  // dynamic LDS per workgroup we allow
 
 __device__ inline uint4 ld16(const void* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
 
+// 16-byte load marked non-temporal (streamed once, not worth caching).
+__device__ inline uint4 ld16_nt(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // The activation slot buffer is never written while a matmul runs, so a
 // wave-uniform address into it may be read through the scalar cache.
-typedef __attribute__((address_space(4))) const uint32_t cu32;
-typedef __attribute__((address_space(4))) const _Float16 chalf;
+typedef __attribute__((address_space(4))) const u32x4 cu32x4;
 
-__device__ inline float half_at(const uint4& v, int i) {
+__device__ inline _Float16 half_bits(uint32_t w, int hi) {
+    return __builtin_bit_cast(_Float16, (uint16_t)(w >> (16 * hi)));
+}
+
+__device__ inline _Float16 half_at(const uint4& v, int i) {
     const uint32_t w = (i >> 1) == 0 ? v.x : (i >> 1) == 1 ? v.y : (i >> 1) == 2 ? v.z : v.w;
-    const uint16_t h = (uint16_t)(w >> (16 * (i & 1)));
-    return (float)__builtin_bit_cast(_Float16, h);
+    return half_bits(w, i & 1);
 }
 
 __device__ inline int live_slot(const int32_t* __restrict__ bidx, int n_live, int t) {
@@ -68,105 +101,175 @@ __device__ inline bool slot_bad(const int32_t* __restrict__ bidx, int t) {
     return s < 0 || s >= kMaxSlots;
 }
 
-__device__ inline float term_fma(int S, float dwf, float dxf, float acc) {
-    const float p = __builtin_fmaf(dwf, dxf, 0.0f);  // exact product
+// One term of the sum: acc + S * (dw * dx), the product of the two binary16
+// scales being exact in fp32.
+__device__ inline float term_fma(int S, _Float16 dw, _Float16 dx, float acc) {
+    const float p = __builtin_fmaf((float)dw, (float)dx, 0.0f);
     return __builtin_fmaf((float)S, p, acc);
+}
+
+struct MmArgs {
+    const uint8_t* wq;    // weights: packed q region
+    const uint16_t* wd;   // weights: packed scale region
+    const uint8_t* xq;    // activation slots: q region (16-row packed layout)
+    const uint16_t* xd;   // activation slots: scale region
+    const int32_t* bidx;  // batch_index
+    float* Y;
+    uint32_t* counters;   // workspace: one arrival counter per row block
+    float* part;          // workspace: split partials [S][row block][tile]
+    int64_t N;
+    int64_t G;
+    int KB, NSC, n_live;
+    int S, KW;            // summation tree: splits, wave slices per split
+    int n_rb;             // row blocks (RG row groups each)
+};
+
+// Super-chunk range [lo, hi) of wave slice k of split s (NSC < 2^16, so 32-bit
+// products are exact).
+__device__ inline void slice_range(int NSC, int S, int KW, int s, int k, int& lo, int& hi) {
+    const int s0 = s * NSC / S, s1 = (s + 1) * NSC / S;
+    const int len = s1 - s0;
+    lo = s0 + k * len / KW;
+    hi = s0 + (k + 1) * len / KW;
+}
+
+// Level 1 of the tree for element e of a tile of E elements: the partial of
+// split s from the KW wave partials red[(s*KW + k)*E + e], k ascending.
+__device__ inline float split_sum(const float* red, int E, int e, int s, int KW) {
+    float p = red[(s * KW) * E + e];
+    for (int k = 1; k < KW; ++k) p += red[(s * KW + k) * E + e];
+    return p;
+}
+
+// Levels 1 and 2 when all S*KW wave partials are in this workgroup's LDS.
+__device__ inline float tree_sum(const float* red, int E, int e, int S, int KW) {
+    float y = split_sum(red, E, e, 0, KW);
+    for (int s = 1; s < S; ++s) y += split_sum(red, E, e, s, KW);
+    return y;
 }
 
 // ------------------------------------------------------------------------
 // MFMA engine
 // ------------------------------------------------------------------------
 
-struct MfmaArgs {
-    const uint8_t* wq;     // packed q region
-    const uint16_t* wd;    // packed scale region
-    const uint8_t* xq;     // activation slot buffer
-    const int32_t* bidx;   // batch_index
-    float* Y;
-    int64_t N;
-    int64_t G;
-    int64_t stride;        // activation slot stride
-    int64_t Kp;
-    int KB, NSC, KS, n_live;
+// The MFMA engine streams its K-slice one chunk (2 blocks, 1 KB per row
+// group) at a time through a ring of D chunks: it dots the oldest chunk and
+// issues the load of the chunk D places ahead, so every wave keeps a small,
+// steady stream of requests in flight (the way a plain streaming read
+// reaches full bandwidth) instead of bursts of whole super-chunks.
+
+// Operands of one chunk for RG row groups, as loaded.
+template <int RG>
+struct Chunk {
+    uint4 w[RG];       // weights: this lane's A operands of blocks 2c, 2c+1
+    uint4 wd[RG];      // rows 4*tq .. 4*tq+3: binary16 scales of blocks 2c, 2c+1
+    uint4 aq;          // activations: B operands of blocks 2c, 2c+1
+    uint32_t dx;       // token lane & 15: binary16 scales of blocks 2c, 2c+1
 };
 
-// One super-chunk (8 blocks) for RG row groups.
-template <int RG, bool TAIL>
-__device__ inline void mfma_step(int sc, int nb, const uint8_t* xa,
-                                 const uint16_t* const xd[4],
-                                 const uint8_t* const wrow[RG],
-                                 const uint16_t* const wdrow[RG],
-                                 float acc[RG][4]) {
-    uint4 aq[4], ad[4], wv[RG][4], wdv[RG];
+// Chunk cg (global chunk index along K) of the weight stream; independent of
+// the live batch, so it can be issued before batch_index has been read.
+template <int RG, bool NTW>
+__device__ inline void load_chunk_w(Chunk<RG>& ch, int cg, const uint8_t* wrow,
+                                    const uint16_t* wdrow, int64_t g_stride_q,
+                                    int64_t g_stride_d) {
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) wv[rg][c] = ld16(wrow[rg] + (int64_t)sc * kScQBytes + c * kChunkBytes);
-        wdv[rg] = ld16(wdrow[rg] + (int64_t)sc * (kScDBytes / 2));
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) aq[c] = ld16(xa + (int64_t)sc * kScValues + c * 64);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ad[r] = ld16(xd[r] + sc * kScBlocks);
-
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        // lanes 0-31 hold block 2c (bytes 16s..16s+15), lanes 32-63 block
-        // 2c+1: swap 8 bytes across the halves so every lane holds its k-slot
-        // of both blocks.
-        const auto s02 = __builtin_amdgcn_permlane32_swap(aq[c].x, aq[c].z, false, false);
-        const auto s13 = __builtin_amdgcn_permlane32_swap(aq[c].y, aq[c].w, false, false);
-        const long xa0 = (long)((uint64_t)s02[0] | ((uint64_t)s13[0] << 32));
-        const long xa1 = (long)((uint64_t)s02[1] | ((uint64_t)s13[1] << 32));
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-            const long w0 = (long)((uint64_t)wv[rg][c].x | ((uint64_t)wv[rg][c].y << 32));
-            const long w1 = (long)((uint64_t)wv[rg][c].z | ((uint64_t)wv[rg][c].w << 32));
-            const v4i zero = {0, 0, 0, 0};
-            const v4i S0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(xa0, w0, zero, 0, 0, 0);
-            const v4i S1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(xa1, w1, zero, 0, 0, 0);
-            const int b0 = 2 * c, b1 = 2 * c + 1;
-            if (!TAIL || b0 < nb) {
-                const float dwf = half_at(wdv[rg], b0);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[rg][r] = term_fma(S0[r], dwf, half_at(ad[r], b0), acc[rg][r]);
-            }
-            if (!TAIL || b1 < nb) {
-                const float dwf = half_at(wdv[rg], b1);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[rg][r] = term_fma(S1[r], dwf, half_at(ad[r], b1), acc[rg][r]);
-            }
-        }
+        const uint8_t* p = wrow + rg * g_stride_q + (int64_t)cg * kChunkBytes;
+        ch.w[rg] = NTW ? ld16_nt(p) : ld16(p);
+        ch.wd[rg] = ld16(wdrow + rg * g_stride_d + (int64_t)cg * (kChunkDBytes / 2));
     }
 }
 
 template <int RG>
-__global__ void __launch_bounds__(1024)
-mm_mfma_kernel(MfmaArgs a) {
-    extern __shared__ float red[];  // [KS][RG][4][64] when KS > 1
-    const int lane = threadIdx.x & 63;
-    const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    const int64_t g0 = (int64_t)blockIdx.x * RG;
-    const int sc0 = (int)(((int64_t)ks * a.NSC) / a.KS);
-    const int sc1 = (int)(((int64_t)(ks + 1) * a.NSC) / a.KS);
+__device__ inline void load_chunk_a(Chunk<RG>& ch, int cg, const uint8_t* xa, const uint16_t* xdp) {
+    ch.aq = ld16(xa + (int64_t)cg * kChunkBytes);
+    ch.dx = *reinterpret_cast<const uint32_t*>(xdp + (int64_t)cg * (kChunkDBytes / 2));
+}
 
-    // activation operand: token lane & 15, 16 bytes at 64c + 16*(lane >> 4)
-    const int sa = live_slot(a.bidx, a.n_live, lane & 15);
-    const uint8_t* xa = a.xq + (int64_t)sa * a.stride + 16 * (lane >> 4);
-    const uint16_t* xd[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int s = live_slot(a.bidx, a.n_live, 4 * (lane >> 4) + r);
-        xd[r] = reinterpret_cast<const uint16_t*>(a.xq + (int64_t)s * a.stride + a.Kp);
-    }
-    const uint8_t* wrow[RG];
-    const uint16_t* wdrow[RG];
+// Dot chunk cg and accumulate: acc[rg][r] is row 4*tq + r of row group rg
+// for token lane & 15.
+template <int RG>
+__device__ inline void mfma_chunk(const Chunk<RG>& ch, int cg, int KB, float acc[RG][4]) {
+    const int b0 = 2 * cg, b1 = 2 * cg + 1;
+    const long xa0 = (long)((uint64_t)ch.aq.x | ((uint64_t)ch.aq.y << 32));
+    const long xa1 = (long)((uint64_t)ch.aq.z | ((uint64_t)ch.aq.w << 32));
+    const _Float16 dx0 = half_bits(ch.dx, 0), dx1 = half_bits(ch.dx, 1);
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-        const int64_t g = min(g0 + rg, a.G - 1);  // past-the-end groups redo the last one
-        wrow[rg] = a.wq + g * a.NSC * kScQBytes + lane * 16;
-        wdrow[rg] = a.wd + g * a.NSC * (kScDBytes / 2) + (lane & 15) * 8;
+        const long w0 = (long)((uint64_t)ch.w[rg].x | ((uint64_t)ch.w[rg].y << 32));
+        const long w1 = (long)((uint64_t)ch.w[rg].z | ((uint64_t)ch.w[rg].w << 32));
+        const v4i zero = {0, 0, 0, 0};
+        const v4i S0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(w0, xa0, zero, 0, 0, 0);
+        const v4i S1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(w1, xa1, zero, 0, 0, 0);
+        // wd[rg]: row 4*tq + r has its block-2c scale in half 2r, block 2c+1 in 2r+1
+        if (b0 < KB) {  // blocks past K are padding
+            acc[rg][0] = term_fma(S0[0], half_bits(ch.wd[rg].x, 0), dx0, acc[rg][0]);
+            acc[rg][1] = term_fma(S0[1], half_bits(ch.wd[rg].y, 0), dx0, acc[rg][1]);
+            acc[rg][2] = term_fma(S0[2], half_bits(ch.wd[rg].z, 0), dx0, acc[rg][2]);
+            acc[rg][3] = term_fma(S0[3], half_bits(ch.wd[rg].w, 0), dx0, acc[rg][3]);
+        }
+        if (b1 < KB) {
+            acc[rg][0] = term_fma(S1[0], half_bits(ch.wd[rg].x, 1), dx1, acc[rg][0]);
+            acc[rg][1] = term_fma(S1[1], half_bits(ch.wd[rg].y, 1), dx1, acc[rg][1]);
+            acc[rg][2] = term_fma(S1[2], half_bits(ch.wd[rg].z, 1), dx1, acc[rg][2]);
+            acc[rg][3] = term_fma(S1[3], half_bits(ch.wd[rg].w, 1), dx1, acc[rg][3]);
+        }
     }
+}
+
+typedef __attribute__((address_space(4))) const int ci32;
+
+// Slot of every token lane, read through the scalar cache (a separate
+// counter from the vector loads, so waiting for it never waits for the
+// weight stream).  Tokens past n_live take token 0's slot; an index outside
+// [0,16) reads slot 0 (its output row is written as NaN).
+__device__ inline void token_slots(const MmArgs& a, int sl[16]) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const int s = ((ci32*)a.bidx)[t < a.n_live ? t : 0];
+        sl[t] = (s >= 0 && s < kMaxSlots) ? s : 0;
+    }
+}
+
+// Loads and stores that are coherent across the whole device (all XCDs)
+// without flushing any cache.
+__device__ inline float coherent_load(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline void coherent_store(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One workgroup per row block (plain: all S*KW waves) or per (row block,
+// split) (SPLIT: KW waves).  LDS: the wave partials red fp32 [waves][RG*256].
+template <int RG, int D, bool NTW, bool SPLIT>
+__global__ void __launch_bounds__(512)
+mm_mfma_kernel(MmArgs a) {
+    extern __shared__ __align__(16) float red[];
+    __shared__ int last_flag;
+    constexpr int E = RG * 256;  // output tile: RG row groups x 16 rows x 16 tokens
+    const int lane = threadIdx.x & 63;
+    const int tq = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int nwaves = SPLIT ? a.KW : a.S * a.KW;
+    const int rb = SPLIT ? (int)(blockIdx.x / a.S) : (int)blockIdx.x;
+    const int split = SPLIT ? (int)(blockIdx.x % a.S) : w / a.KW;
+    int sc0, sc1;
+    slice_range(a.NSC, a.S, a.KW, split, SPLIT ? w : w % a.KW, sc0, sc1);
+    const int c_lo = 4 * sc0, c_hi = 4 * sc1;  // this wave's chunks
+
+    // weights: RG consecutive row groups; the last row block may start
+    // earlier (gbase < g0) so that every load stays inside the buffer, and
+    // then stores only the groups from g0 on
+    const int64_t g0 = (int64_t)rb * RG;
+    const int64_t gbase = min(g0, a.G - RG);
+    const int64_t gq = (int64_t)a.NSC * kScQBytes;              // bytes per row group
+    const int64_t gd = (int64_t)a.NSC * 4 * (kChunkDBytes / 2);  // halves per row group
+    const uint8_t* wrow = a.wq + gbase * gq + lane * 16;
+    const uint16_t* wdrow = a.wd + gbase * gd + tq * 8;
+    const int gskip = (int)(g0 - gbase);
 
     float acc[RG][4];
 #pragma unroll
@@ -174,37 +277,111 @@ mm_mfma_kernel(MfmaArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[rg][r] = 0.0f;
 
-    const int sc_full = min(sc1, a.KB / kScBlocks);
-    int sc = sc0;
-    for (; sc < sc_full; ++sc) mfma_step<RG, false>(sc, kScBlocks, xa, xd, wrow, wdrow, acc);
-    if (sc < sc1) mfma_step<RG, true>(sc, a.KB - sc * kScBlocks, xa, xd, wrow, wdrow, acc);
+    // the first weights go out before anything waits for batch_index
+    Chunk<RG> ring[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        if (c_lo + i < c_hi) load_chunk_w<RG, NTW>(ring[i], c_lo + i, wrow, wdrow, gq, gd);
 
-    if (a.KS == 1) {
+    int sl[16];
+    token_slots(a, sl);
+    // this lane's token: B operand at k-slot tq, and its scales
+    int sa = sl[0];
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
+    for (int t = 1; t < 16; ++t) sa = (lane & 15) == t ? sl[t] : sa;
+    const uint8_t* xa = a.xq + (tq * 16 + sa) * 16;
+    const uint16_t* xdp = a.xd + sa * 2;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * (lane >> 4) + r;
-                const int64_t n = (g0 + rg) * kRowsPerGroup + (lane & 15);
-                if (t < a.n_live && n < a.N)
-                    a.Y[(int64_t)t * a.N + n] = slot_bad(a.bidx, t) ? __builtin_nanf("") : acc[rg][r];
-            }
-        return;
+    for (int i = 0; i < D; ++i)
+        if (c_lo + i < c_hi) load_chunk_a<RG>(ring[i], c_lo + i, xa, xdp);
+
+    // dot the oldest chunk, load the one D ahead
+    int c = c_lo;
+    for (; c + 2 * D <= c_hi; c += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            mfma_chunk<RG>(ring[i], c + i, a.KB, acc);
+            load_chunk_w<RG, NTW>(ring[i], c + i + D, wrow, wdrow, gq, gd);
+            load_chunk_a<RG>(ring[i], c + i + D, xa, xdp);
+        }
     }
+#pragma unroll
+    for (int i = 0; i < D; ++i) {  // fewer than 2D chunks left, D in the ring
+        if (c + i < c_hi) {
+            mfma_chunk<RG>(ring[i], c + i, a.KB, acc);
+            if (c + i + D < c_hi) {
+                load_chunk_w<RG, NTW>(ring[i], c + i + D, wrow, wdrow, gq, gd);
+                load_chunk_a<RG>(ring[i], c + i + D, xa, xdp);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        if (c + D + i < c_hi) mfma_chunk<RG>(ring[i], c + D + i, a.KB, acc);
+
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[((ks * RG + rg) * 4 + r) * 64 + lane] = acc[rg][r];
+        for (int r = 0; r < 4; ++r) red[(w * RG + rg) * 256 + r * 64 + lane] = acc[rg][r];
     __syncthreads();
-    for (int e = threadIdx.x; e < RG * 256; e += a.KS * 64) {
-        float y = red[e];
-        for (int k = 1; k < a.KS; ++k) y += red[k * RG * 256 + e];
+
+    const int nthreads = nwaves * 64;
+    if (!SPLIT) {
+        for (int e = threadIdx.x; e < E; e += nthreads) {
+            const float y = tree_sum(red, E, e, a.S, a.KW);
+            const int rg = e >> 8, r = (e >> 6) & 3, ln = e & 63;
+            const int t = ln & 15;
+            const int64_t n = (gbase + rg) * kRowsPerGroup + 4 * (ln >> 4) + r;
+            if (rg >= gskip && t < a.n_live && n < a.N)
+                a.Y[(int64_t)t * a.N + n] = slot_bad(a.bidx, t) ? __builtin_nanf("") : y;
+        }
+        return;
+    }
+    // level 1 of this split, published in the workspace.  The partials are
+    // written with device-coherent stores and the wait below makes them
+    // complete before the counter moves, so no cache has to be flushed; the
+    // last split reads them back with device-coherent loads.
+    float* mine = a.part + ((int64_t)split * a.n_rb + rb) * E;
+    for (int e = threadIdx.x; e < E; e += nthreads) coherent_store(mine + e, split_sum(red, E, e, 0, a.KW));
+    // every thread waits for its own stores to complete before the barrier,
+    // so the counter can only move once the whole partial is in place
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        last_flag = __hip_atomic_fetch_add(a.counters + rb, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(a.S - 1);
+    __syncthreads();
+    if (!last_flag) return;
+    // the last split to arrive: level 2 in split order, then rearm the counter
+    for (int e = threadIdx.x; e < E; e += nthreads) {
+        float y = coherent_load(a.part + (int64_t)rb * E + e);
+        for (int s = 1; s < a.S; ++s) y += coherent_load(a.part + ((int64_t)s * a.n_rb + rb) * E + e);
         const int rg = e >> 8, r = (e >> 6) & 3, ln = e & 63;
-        const int t = 4 * (ln >> 4) + r;
-        const int64_t n = (g0 + rg) * kRowsPerGroup + (ln & 15);
-        if (t < a.n_live && n < a.N)
+        const int t = ln & 15;
+        const int64_t n = (gbase + rg) * kRowsPerGroup + 4 * (ln >> 4) + r;
+        if (rg >= gskip && t < a.n_live && n < a.N)
             a.Y[(int64_t)t * a.N + n] = slot_bad(a.bidx, t) ? __builtin_nanf("") : y;
     }
+    if (threadIdx.x == 0) __hip_atomic_store(a.counters + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+size_t mfma_lds_bytes(const MmArgs& a, int rg, bool split) {
+    const int waves = split ? a.KW : a.S * a.KW;
+    return (size_t)waves * rg * 256 * sizeof(float);
+}
+
+int mfma_max_waves(int) { return 8; }  // 512 threads: 256 VGPRs per lane
+
+template <int RG, int D, bool NTW, bool SPLIT>
+hipError_t launch_mfma(const MmArgs& a, hipStream_t st) {
+    const int waves = SPLIT ? a.KW : a.S * a.KW;
+    const size_t lds = mfma_lds_bytes(a, RG, SPLIT);
+    if (lds > kMaxLds || waves > mfma_max_waves(RG) || a.G < RG) return hipErrorInvalidValue;
+    const unsigned grid = (unsigned)(SPLIT ? (int64_t)a.n_rb * a.S : a.n_rb);
+    hipLaunchKernelGGL((mm_mfma_kernel<RG, D, NTW, SPLIT>), dim3(grid), dim3(64 * waves), lds, st, a);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------
@@ -213,94 +390,70 @@ mm_mfma_kernel(MfmaArgs a) {
 
 template <int NT, bool TAIL>
 __device__ inline void dot4_step(int sc, int nb, const uint8_t* wrow,
-                                 const uint16_t* wdrow,
-                                 const uint8_t* const xrow[NT], int64_t Kp,
-                                 float acc[NT]) {
-    const uint4 wdv = ld16(wdrow + (int64_t)sc * (kScDBytes / 2));
-    // token scales of the 8 blocks: 4 dwords of two halves each, scalar loads
-    uint32_t dxw[NT][4];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        cu32* dp = (cu32*)(xrow[t] + Kp + (int64_t)sc * kScBlocks * 2);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dxw[t][i] = dp[i];
-    }
+                                 const uint16_t* wdrow, const MmArgs& a,
+                                 const int slot[NT], float acc[NT]) {
 #pragma unroll 1
     for (int c = 0; c < 4; ++c) {
         if (TAIL && 2 * c >= nb) break;
+        const int64_t chunk = (int64_t)sc * 4 + c;
         uint4 w[4];  // [k-slot]: this row's 8 bytes of blocks 2c and 2c+1
 #pragma unroll
-        for (int s = 0; s < 4; ++s) w[s] = ld16(wrow + (int64_t)sc * kScQBytes + c * kChunkBytes + s * 256);
+        for (int k = 0; k < 4; ++k) w[k] = ld16(wrow + chunk * kChunkBytes + k * 256);
+        const uint32_t wdc = *reinterpret_cast<const uint32_t*>(wdrow + chunk * (kChunkDBytes / 2));
+        const _Float16 dw0 = half_bits(wdc, 0), dw1 = half_bits(wdc, 1);
+        const bool has1 = !TAIL || 2 * c + 1 < nb;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int bb = 2 * c + h;
-            if (TAIL && bb >= nb) continue;
-            const int64_t b = (int64_t)sc * kScBlocks + bb;
-            const float dwf = half_at(wdv, bb);
+        for (int t = 0; t < NT; ++t) {
+            const uint8_t* xs = a.xq + chunk * kChunkBytes + slot[t] * 16;
+            int S0 = 0, S1 = 0;
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                cu32* ap = (cu32*)(xrow[t] + b * kBlock);
-                int S = 0;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int p4 = slot_pos(s) / 4;
-                    const uint32_t wlo = h ? w[s].z : w[s].x;
-                    const uint32_t whi = h ? w[s].w : w[s].y;
-                    S = __builtin_amdgcn_sdot4((int)wlo, (int)ap[p4], S, false);
-                    S = __builtin_amdgcn_sdot4((int)whi, (int)ap[p4 + 1], S, false);
-                }
-                // dxw[t][c] holds the halves of blocks 2c (low) and 2c+1 (high)
-                uint32_t dsel = dxw[t][0];
-#pragma unroll
-                for (int i = 1; i < 4; ++i) dsel = (c == i) ? dxw[t][i] : dsel;
-                const uint16_t dh = (uint16_t)(dsel >> (16 * h));
-                acc[t] = term_fma(S, dwf, (float)__builtin_bit_cast(_Float16, dh), acc[t]);
+            for (int k = 0; k < 4; ++k) {
+                const u32x4 x = *(cu32x4*)(xs + k * 256);
+                S0 = __builtin_amdgcn_sdot4((int)w[k].x, (int)x.x, S0, false);
+                S0 = __builtin_amdgcn_sdot4((int)w[k].y, (int)x.y, S0, false);
+                S1 = __builtin_amdgcn_sdot4((int)w[k].z, (int)x.z, S1, false);
+                S1 = __builtin_amdgcn_sdot4((int)w[k].w, (int)x.w, S1, false);
             }
+            const uint32_t dv = *(const __attribute__((address_space(4))) uint32_t*)(
+                a.xd + (chunk * 16 + slot[t]) * 2);
+            acc[t] = term_fma(S0, dw0, half_bits(dv, 0), acc[t]);
+            if (has1) acc[t] = term_fma(S1, dw1, half_bits(dv, 1), acc[t]);
         }
     }
 }
 
 template <int NT>
 __global__ void __launch_bounds__(1024)
-mm_dot4_kernel(MfmaArgs a) {
-    extern __shared__ float red[];  // [KS][NT][64] when KS > 1
+mm_dot4_kernel(MmArgs a) {
+    extern __shared__ float red[];  // wave partials [S*KW][NT*64]
+    constexpr int E = NT * 64;
     const int lane = threadIdx.x & 63;
-    const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int nwaves = a.S * a.KW;
+    int sc0, sc1;
+    slice_range(a.NSC, a.S, a.KW, w / a.KW, w % a.KW, sc0, sc1);
     const int64_t g0 = (int64_t)blockIdx.x * 4;
-    const int sc0 = (int)(((int64_t)ks * a.NSC) / a.KS);
-    const int sc1 = (int)(((int64_t)(ks + 1) * a.NSC) / a.KS);
     const int64_t g = min(g0 + (lane >> 4), a.G - 1);
     const int j = lane & 15;
     const uint8_t* wrow = a.wq + g * a.NSC * kScQBytes + j * 16;
-    const uint16_t* wdrow = a.wd + g * a.NSC * (kScDBytes / 2) + j * 8;
-    const uint8_t* xrow[NT];
+    const uint16_t* wdrow = a.wd + g * a.NSC * 4 * (kChunkDBytes / 2) + j * 2;
+    int slot[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const int s = __builtin_amdgcn_readfirstlane(live_slot(a.bidx, a.n_live, t));
-        xrow[t] = a.xq + (int64_t)s * a.stride;
-    }
+    for (int t = 0; t < NT; ++t) slot[t] = __builtin_amdgcn_readfirstlane(live_slot(a.bidx, a.n_live, t));
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
 
     const int sc_full = min(sc1, a.KB / kScBlocks);
     int sc = sc0;
-    for (; sc < sc_full; ++sc) dot4_step<NT, false>(sc, kScBlocks, wrow, wdrow, xrow, a.Kp, acc);
-    if (sc < sc1) dot4_step<NT, true>(sc, a.KB - sc * kScBlocks, wrow, wdrow, xrow, a.Kp, acc);
+    for (; sc < sc_full; ++sc) dot4_step<NT, false>(sc, kScBlocks, wrow, wdrow, a, slot, acc);
+    if (sc < sc1) dot4_step<NT, true>(sc, a.KB - sc * kScBlocks, wrow, wdrow, a, slot, acc);
 
-    const int64_t n = (g0 + (lane >> 4)) * kRowsPerGroup + j;
-    if (a.KS == 1) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-            if (n < a.N) a.Y[(int64_t)t * a.N + n] = slot_bad(a.bidx, t) ? __builtin_nanf("") : acc[t];
-        return;
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) red[(ks * NT + t) * 64 + lane] = acc[t];
+    for (int t = 0; t < NT; ++t) red[w * E + t * 64 + lane] = acc[t];
     __syncthreads();
-    for (int e = threadIdx.x; e < NT * 64; e += a.KS * 64) {
-        float y = red[e];
-        for (int k = 1; k < a.KS; ++k) y += red[k * NT * 64 + e];
+    for (int e = threadIdx.x; e < E; e += nwaves * 64) {
+        const float y = tree_sum(red, E, e, a.S, a.KW);
         const int t = e >> 6, ln = e & 63;
         const int64_t nn = (g0 + (ln >> 4)) * kRowsPerGroup + (ln & 15);
         if (nn < a.N) a.Y[(int64_t)t * a.N + nn] = slot_bad(a.bidx, t) ? __builtin_nanf("") : y;
@@ -308,14 +461,16 @@ mm_dot4_kernel(MfmaArgs a) {
 }
 
 template <int NT>
-hipError_t launch_dot4_nt(const MfmaArgs& a, hipStream_t st) {
+hipError_t launch_dot4_nt(const MmArgs& a, hipStream_t st) {
     const unsigned grid = (unsigned)((a.G + 3) / 4);
-    const size_t lds = a.KS > 1 ? (size_t)a.KS * NT * 64 * sizeof(float) : 0;
-    hipLaunchKernelGGL(mm_dot4_kernel<NT>, dim3(grid), dim3(64 * a.KS), lds, st, a);
+    const int waves = a.S * a.KW;
+    if (waves > kMaxKs) return hipErrorInvalidValue;
+    const size_t lds = (size_t)waves * NT * 64 * sizeof(float);
+    hipLaunchKernelGGL(mm_dot4_kernel<NT>, dim3(grid), dim3(64 * waves), lds, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_dot4(const MfmaArgs& a, hipStream_t st) {
+hipError_t launch_dot4(const MmArgs& a, hipStream_t st) {
     switch (a.n_live) {
         case 1: return launch_dot4_nt<1>(a, st);
         case 2: return launch_dot4_nt<2>(a, st);
@@ -340,39 +495,87 @@ hipError_t launch_dot4(const MfmaArgs& a, hipStream_t st) {
 }  // namespace
 
 Tiling choose_tiling(const Shape& s) {
-    // Enough waves to keep ~4096 weight streams in flight across 256 CUs,
-    // never more K-slices than super-chunks or than a workgroup can hold.
+    // Rules measured on MI355X over the model-shaped matrices (K 5120..18432,
+    // N 5120..151936):
+    //  * two row groups per wave (32 rows per activation load) once there are
+    //    enough row groups to fill the machine, else one;
+    //  * split K across workgroups until there are >= 4 workgroups per CU
+    //    (256 CUs), each split keeping >= 2 super-chunks;
+    //  * wave slices per split for about 4096 waves in the grid, at most 8
+    //    waves per workgroup and >= 1 super-chunk per wave.
     Tiling t;
-    int64_t ks = (4096 + s.G - 1) / s.G;
-    ks = std::min<int64_t>(ks, std::min<int64_t>(kMaxKs, s.NSC));
-    t.ks = (int)std::max<int64_t>(ks, 1);
+    t.rg = s.G >= 1024 ? 2 : 1;
+    const int64_t n_rb = (s.G + t.rg - 1) / t.rg;
+    t.splits = 1;
+    while (t.splits < 8 && n_rb * t.splits < 1024 && s.NSC >= 4 * t.splits) t.splits *= 2;
+    const int max_waves = 8;  // 512-thread workgroups
+    int64_t kw = (4096 + n_rb * t.splits - 1) / (n_rb * t.splits);
+    kw = std::min<int64_t>(kw, max_waves / t.splits);
+    kw = std::min<int64_t>(kw, s.NSC / t.splits);
+    t.kw = (int)std::max<int64_t>(kw, 1);
+    t.nt_weights = true;
+#ifdef Q8_TUNING
+    // measurement builds only: override the tiling from the environment
+    if (const char* e = getenv("Q8_RG")) t.rg = atoi(e) == 2 ? 2 : 1;
+    if (const char* e = getenv("Q8_S")) t.splits = std::max(1, atoi(e));
+    if (const char* e = getenv("Q8_KW")) t.kw = std::max(1, atoi(e));
+    if (const char* e = getenv("Q8_NTW")) t.nt_weights = atoi(e) != 0;
+#endif
     return t;
+}
+
+// Row groups per wave actually launched (a matrix with fewer row groups than
+// asked for runs one per wave).
+int launch_rg(const Shape& s, const Tiling& t) { return s.G >= t.rg ? t.rg : 1; }
+
+size_t workspace_bytes(const Shape& s, const Tiling& t) {
+    if (t.splits <= 1) return 0;
+    const int rg = launch_rg(s, t);
+    const int64_t n_rb = (s.G + rg - 1) / rg;
+    const int64_t counters = align_up(n_rb * 4, 256);
+    return (size_t)(counters + (int64_t)t.splits * n_rb * rg * 256 * 4);
 }
 
 hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
                          const int32_t* batch_index, int n_live,
                          const Shape& s, const Tiling& t, float* Y,
-                         hipStream_t st) {
-    MfmaArgs a;
+                         void* workspace, hipStream_t st) {
+    MmArgs a;
     a.wq = Wq;
     a.wd = reinterpret_cast<const uint16_t*>(Wq + s.q_bytes);
     a.xq = Xq;
+    a.xd = reinterpret_cast<const uint16_t*>(Xq + s.act_q_bytes);
     a.bidx = batch_index;
     a.Y = Y;
     a.N = s.N;
     a.G = s.G;
-    a.stride = s.stride;
-    a.Kp = s.Kp;
     a.KB = (int)s.KB;
     a.NSC = (int)s.NSC;
-    a.KS = t.ks;
     a.n_live = n_live;
+    a.S = t.splits;
+    a.KW = t.kw;
+    if (a.S * a.KW > a.NSC) return hipErrorInvalidValue;
     if (e == Engine::kDot4) return launch_dot4(a, st);
-    constexpr int RG = 1;
-    const unsigned grid = (unsigned)((s.G + RG - 1) / RG);
-    const size_t lds = t.ks > 1 ? (size_t)t.ks * RG * 256 * sizeof(float) : 0;
-    hipLaunchKernelGGL(mm_mfma_kernel<RG>, dim3(grid), dim3(64 * t.ks), lds, st, a);
-    return hipGetLastError();
+    const int rg = launch_rg(s, t);
+    a.n_rb = (int)((s.G + rg - 1) / rg);
+    const bool split = workspace != nullptr && t.splits > 1;
+    a.counters = nullptr;
+    a.part = nullptr;
+    if (split) {
+        a.counters = static_cast<uint32_t*>(workspace);
+        a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                          align_up((int64_t)a.n_rb * 4, 256));
+    }
+#define Q8_LAUNCH(R, N, P) return launch_mfma<R, kRing, N, P>(a, st)
+    if (rg == 2) {
+        if (split) { if (t.nt_weights) Q8_LAUNCH(2, true, true); Q8_LAUNCH(2, false, true); }
+        if (t.nt_weights) Q8_LAUNCH(2, true, false);
+        Q8_LAUNCH(2, false, false);
+    }
+    if (split) { if (t.nt_weights) Q8_LAUNCH(1, true, true); Q8_LAUNCH(1, false, true); }
+    if (t.nt_weights) Q8_LAUNCH(1, true, false);
+    Q8_LAUNCH(1, false, false);
+#undef Q8_LAUNCH
 }
 
 }  // namespace q8

@@ -6,6 +6,7 @@
 // -- the narrow-batch matmul" (32-weight blocks, pre-quantised activations),
 // read as the GGUF q8_0 block: d = absmax/127 in binary32, q = round half away
 // from zero of x/d (IEEE division), clamped to +-127, d stored as binary16.
+// The activation slot buffer uses the packed layout of a 16-row matrix.
 //
 // Thread mapping, all kernels: one lane per 8-value segment, 4 consecutive
 // lanes per 32-value block, consecutive blocks of a row on consecutive lane
@@ -54,12 +55,12 @@ __device__ inline int64_t packed_q_offset(int64_t row, int64_t blk, int seg,
 }
 
 // Index (in halves) of the scale of block `blk` of row `row` in the packed
-// scale region.
+// scale region: [group][chunk][16 rows][2 blocks].
 __device__ inline int64_t packed_d_index(int64_t row, int64_t blk, int64_t NSC) {
     const int64_t g = row >> 4;
     const int j = (int)(row & 15);
-    const int64_t sc = blk >> 3;
-    return ((g * NSC + sc) * 16 + j) * 8 + (blk & 7);
+    const int64_t c = blk >> 1;
+    return ((g * 4 * NSC + c) * 16 + j) * 2 + (blk & 1);
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -108,19 +109,21 @@ unpack_weights_kernel(const uint8_t* __restrict__ wq, const uint16_t* __restrict
     if (ix.seg == 0) d16[ix.row * KB + ix.blk] = wd[packed_d_index(ix.row, ix.blk, NSC)];
 }
 
+// Activations go to the packed layout of a 16-row matrix (row = slot); only
+// rows < n_rows are written.
 __global__ void __launch_bounds__(kThreads)
 quantize_acts_kernel(const float* __restrict__ X, int64_t K, int64_t KB,
-                     int64_t NSC, int64_t Kp, int64_t stride, int64_t total,
-                     uint8_t* __restrict__ xq) {
+                     int64_t NSC, int64_t total, uint8_t* __restrict__ xq,
+                     uint16_t* __restrict__ xd) {
     const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (tid >= total) return;
     const SegIndex ix = seg_index(tid, NSC * kScBlocks);
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (ix.blk < KB) load8(X + ix.row * K + ix.blk * kBlock + ix.seg * 8, v);
     const QuantSeg r = quantize_segment(v);
-    uint8_t* slot = xq + ix.row * stride;
-    *reinterpret_cast<uint2*>(slot + ix.blk * kBlock + ix.seg * 8) = make_uint2(r.lo, r.hi);
-    if (ix.seg == 0) reinterpret_cast<uint16_t*>(slot + Kp)[ix.blk] = r.d16;
+    *reinterpret_cast<uint2*>(xq + packed_q_offset(ix.row, ix.blk, ix.seg, NSC)) =
+        make_uint2(r.lo, r.hi);
+    if (ix.seg == 0) xd[packed_d_index(ix.row, ix.blk, NSC)] = r.d16;
 }
 
 inline unsigned grid_for(int64_t total) {
@@ -159,8 +162,9 @@ hipError_t launch_unpack_weights(const uint8_t* Wq, const Shape& s, int8_t* q,
 hipError_t launch_quantize_acts(const float* X, int n_rows, const Shape& s,
                                 uint8_t* Xq, hipStream_t st) {
     const int64_t total = (int64_t)n_rows * s.NSC * kScBlocks * 4;
+    uint16_t* xd = reinterpret_cast<uint16_t*>(Xq + s.act_q_bytes);
     hipLaunchKernelGGL(quantize_acts_kernel, dim3(grid_for(total)), dim3(kThreads),
-                       0, st, X, s.K, s.KB, s.NSC, s.Kp, s.stride, total, Xq);
+                       0, st, X, s.K, s.KB, s.NSC, total, Xq, xd);
     return hipGetLastError();
 }
 

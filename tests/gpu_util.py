@@ -56,20 +56,18 @@ def gpu_quantize_acts(X: np.ndarray, Xq: torch.Tensor | None = None) -> torch.Te
 
 
 def slots_host(Xq: torch.Tensor, K: int):
-    """(q int8 [16][K], d16 uint16 [16][K/32]) read from the public layout."""
+    """(q int8 [16][K], d16 uint16 [16][K/32]) of every slot, read back
+    through the library's unpack kernel."""
+    q, d = q8().read_act_slots(Xq, K)
     torch.cuda.synchronize()
-    q, d = q8().split_act_slots(Xq, K)
     return q.cpu().numpy(), d.cpu().numpy().view(np.uint16)
 
 
-def write_slots(Xq: torch.Tensor, K: int, q: np.ndarray, d16: np.ndarray,
-                slots=None) -> None:
-    """Craft slots directly in the public layout."""
-    qv, dv = q8().split_act_slots(Xq, K)
-    slots = range(q.shape[0]) if slots is None else slots
-    for i, s in enumerate(slots):
-        qv[s].copy_(torch.from_numpy(np.ascontiguousarray(q[i])))
-        dv[s].copy_(torch.from_numpy(np.ascontiguousarray(d16[i]).view(np.int16)))
+def write_slots(Xq: torch.Tensor, K: int, q: np.ndarray, d16: np.ndarray) -> None:
+    """Write all 16 slots from canonical q8_0 arrays."""
+    q8().write_act_slots(Xq, K, to_dev(q.astype(np.int8)),
+                         to_dev(d16.astype(np.uint16).view(np.int16)))
+    torch.cuda.synchronize()
 
 
 def gpu_matmul(Wq, Xq, bi: np.ndarray, N: int, K: int, path: int = 0) -> np.ndarray:
@@ -77,6 +75,16 @@ def gpu_matmul(Wq, Xq, bi: np.ndarray, N: int, K: int, path: int = 0) -> np.ndar
     bi_d = to_dev(np.asarray(bi, dtype=np.int32))
     Y = torch.empty((bi_d.numel(), N), dtype=torch.float32, device="cuda")
     m.q8_matmul_narrow_path(Wq, Xq, bi_d, bi_d.numel(), N, K, Y, path)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy()
+
+
+def gpu_matmul_ws(Wq, Xq, bi: np.ndarray, N: int, K: int, ws) -> np.ndarray:
+    """The workspace entry point (split execution) on a given workspace."""
+    m = q8()
+    bi_d = to_dev(np.asarray(bi, dtype=np.int32))
+    Y = torch.empty((bi_d.numel(), N), dtype=torch.float32, device="cuda")
+    m.q8_matmul_narrow_ws(Wq, Xq, bi_d, bi_d.numel(), N, K, Y, ws)
     torch.cuda.synchronize()
     return Y.cpu().numpy()
 

@@ -29,7 +29,7 @@ def test_header_declares_the_abi():
     names = header_functions()
     for core in ("q8_pack_weights", "q8_quantize_acts", "q8_matmul_narrow"):
         assert core in names
-    assert len(names) == 11, names
+    assert len(names) == 12, names
 
 
 def test_every_declared_symbol_is_exported(q8):
@@ -63,11 +63,8 @@ def test_layout_sizes(q8, N, K):
     G = -(-N // 16)
     NSC = -(-K // 256)
     assert q8.q8_packed_weight_bytes(N, K) == G * NSC * (4096 + 256)
-    Kp = NSC * 256
-    stride = -(-(Kp + 2 * Kp // 32) // 256) * 256
-    assert q8.q8_act_slot_stride(K) == stride
-    assert stride % 256 == 0 and stride >= K + 2 * (K // 32)
-    assert q8.q8_act_buffer_bytes(K) == 16 * stride
+    # the slot buffer is the packed form of a 16-row matrix
+    assert q8.q8_act_buffer_bytes(K) == q8.q8_packed_weight_bytes(16, K) == NSC * 4352
 
 
 def test_packed_size_is_weight_bytes_plus_padding(q8):
@@ -81,9 +78,8 @@ def test_invalid_shapes_have_no_size(q8, N, K):
     assert q8.q8_packed_weight_bytes(N, K) == 0
 
 
-def test_invalid_k_has_no_slot_stride(q8):
-    assert q8.q8_act_slot_stride(0) == 0
-    assert q8.q8_act_slot_stride(33) == 0
+def test_invalid_k_has_no_slot_buffer(q8):
+    assert q8.q8_act_buffer_bytes(0) == 0
     assert q8.q8_act_buffer_bytes(33) == 0
 
 
@@ -139,6 +135,25 @@ def test_other_entry_points_reject_invalid_arguments(q8):
     assert lib.q8_quantize_acts(P, 4, 65, P, None) == bad
     assert lib.q8_quantize_acts(P + 4, 4, 64, P, None) == bad
     assert lib.q8_quantize_acts(P, 4, 64, None, None) == bad
+
+
+def test_workspace_sizes(q8):
+    # small-N shapes are split across workgroups and need a workspace; the
+    # 151936-row head is not split
+    assert q8.q8_matmul_workspace_bytes(5120, 5120) > 0
+    assert q8.q8_matmul_workspace_bytes(151936, 5120) == 0
+    assert q8.q8_matmul_workspace_bytes(0, 5120) == 0
+    assert q8.q8_matmul_workspace_bytes(16, 32) == 0  # one super-chunk: no split
+
+
+def test_ws_entry_point_rejects_a_missing_or_small_workspace(q8):
+    lib = q8.library()
+    bad = q8.Q8_ERR_INVALID_ARG
+    need = q8.q8_matmul_workspace_bytes(5120, 5120)
+    assert lib.q8_matmul_narrow_ws(P, P, P, 4, 5120, 5120, P, None, need, None) == bad
+    assert lib.q8_matmul_narrow_ws(P, P, P, 4, 5120, 5120, P, P, need - 1, None) == bad
+    assert lib.q8_matmul_narrow_ws(P, P, P, 4, 5120, 5120, P, P + 16, need, None) == bad
+    assert lib.q8_matmul_narrow_ws(P, P, P, 0, 5120, 5120, P, P, need, None) == bad
 
 
 def test_binding_raises_on_rejected_call(q8):

@@ -1,0 +1,49 @@
+"""Host-side pieces of bench.py (no GPU)."""
+
+import os
+
+import pytest
+
+import bench
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "ds4_measured.txt")
+
+
+def _rows():
+    for line in open(GOLDEN):
+        if line.strip() and not line.startswith("#"):
+            path, n, ms, sp = line.split()
+            yield path, int(n), (None if ms == "-" else float(ms)), float(sp)
+
+
+def test_speedup_formula_reproduces_the_printed_table():
+    rows = list(_rows())
+    t1 = [r for r in rows if r[0] == "single"][0][2]
+    checked = 0
+    for path, n, ms, sp in rows:
+        if ms is None:
+            continue
+        # printed to two decimals (0.6252 is printed 0.62 on the page)
+        assert abs(bench.speedup_vs_single(t1, ms, n) - sp) <= 0.01, (path, n)
+        checked += 1
+    assert checked == 5
+
+
+def test_matmul_bytes_match_the_packed_format():
+    # weights 34 B per 32, activations 34 B per block per token
+    assert bench.matmul_bytes(7168, 5120, 1) == 7168 * 160 * 34 + 160 * 34 + 4 + 4 * 7168
+    b16 = bench.matmul_bytes(151936, 5120, 16)
+    assert abs(b16 / 1e6 - 836.34) < 0.01
+    assert abs(bench.matmul_bytes(5120, 17408, 16) / 1e6 - 95.32) < 0.01
+
+
+def test_step_bytes_of_the_qwen3_layer():
+    mats = wl.WORKLOADS["qwen3_layer"].matrices
+    mm = sum(bench.matmul_bytes(m.N, m.K, 16) for m in mats)
+    assert abs(mm / 1e6 - (39.54 + 28.27 + 191.71 + 95.32)) < 0.05
+    assert bench.step_bytes(mats, 16) > mm
+
+
+def test_more_than_one_gpu_is_refused():
+    assert bench.main(["--gpus", "2"]) == 2

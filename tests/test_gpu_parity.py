@@ -12,9 +12,9 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_util import (gpu_matmul, gpu_pack, gpu_pack_q, gpu_quantize_acts,
-                      gpu_unpack, sample_rows, slots_host, to_dev, within_tau,
-                      write_slots)
+from gpu_util import (gpu_matmul, gpu_matmul_ws, gpu_pack, gpu_pack_q,
+                      gpu_quantize_acts, gpu_unpack, sample_rows, slots_host,
+                      to_dev, within_tau, write_slots)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,25 +51,35 @@ def test_quantize_acts_bit_exact(K):
     qo, do = oracle.quantize_rows(X)
     assert np.array_equal(q, qo)
     assert np.array_equal(d, do)
-    # padding of each slot is written as zero
-    raw = Xq.view(16, -1).cpu().numpy()
-    Kp = (K + 255) // 256 * 256
-    assert not raw[:, K:Kp].any()
-    assert not raw[:, Kp + 2 * (K // 32):Kp + Kp // 16].any()
+
+
+def test_quantize_acts_pads_with_zero():
+    """Blocks past K inside the last 256-value super-chunk are written as
+    zero (q and scale), whatever the buffer held before."""
+    import quantized_weight_streaming_q8_amd as q8
+    K = 4128  # 129 blocks: 7 padding blocks in the last super-chunk
+    Xq = q8.empty_act_slots(K)
+    Xq.fill_(0x5A)
+    gpu_quantize_acts(_ragged_x(K, seed=2), Xq)
+    Kp = 17 * 256
+    qp, dp = slots_host(Xq, Kp)  # read the padded width back
+    assert not qp[:, K:].any() and not dp[:, K // 32:].any()
 
 
 def test_quantize_acts_partial_rows_leave_other_slots():
     K = 1024
     import quantized_weight_streaming_q8_amd as q8
     Xq = q8.empty_act_slots(K)
-    Xq.fill_(0x5A)
+    rng = np.random.default_rng(3)
+    q0 = rng.integers(-128, 128, size=(16, K)).astype(np.int8)
+    d0 = rng.integers(0, 0x7c00, size=(16, K // 32)).astype(np.uint16)
+    write_slots(Xq, K, q0, d0)
     X = _ragged_x(K, seed=1)[:5]
     gpu_quantize_acts(X, Xq)
-    raw = Xq.view(16, -1).cpu().numpy()
-    assert np.all(raw[5:] == 0x5A)
     q, d = slots_host(Xq, K)
     qo, do = oracle.quantize_rows(X)
     assert np.array_equal(q[:5], qo) and np.array_equal(d[:5], do)
+    assert np.array_equal(q[5:], q0[5:]) and np.array_equal(d[5:], d0[5:])
 
 
 # ------------------------------------------------------------------- packer
@@ -119,12 +129,15 @@ def _oracle_y(W, X, bi, rows=None):
 
 
 @pytest.mark.parametrize("N,K", [(1, 32), (17, 288), (15, 2080), (100, 800),
-                                 (16, 256), (33, 4128), (768, 768), (40, 17408)])
+                                 (16, 256), (33, 4128), (768, 768), (40, 17408),
+                                 (1000, 5120), (5120, 2080)])
 def test_matmul_ragged_shapes(N, K):
     rng = np.random.default_rng(N + K)
     W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
     X = _ragged_x(K, seed=K + 1)
     Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
+    import quantized_weight_streaming_q8_amd as q8
+    ws = q8.zeroed_workspace(N, K)
     for bi in (np.array([0]), np.array([3, 3, 9]), rng.permutation(16),
                np.array([15, 2, 2, 7, 0, 11, 5])):
         bi = bi.astype(np.int32)
@@ -134,6 +147,8 @@ def test_matmul_ragged_shapes(N, K):
         assert ok, (N, K, bi, worst)
         Yd = gpu_matmul(Wq, Xq, bi, N, K, DOT4)
         assert np.array_equal(Ym.view(np.uint32), Yd.view(np.uint32)), (N, K, bi)
+        Yw = gpu_matmul_ws(Wq, Xq, bi, N, K, ws)
+        assert np.array_equal(Ym.view(np.uint32), Yw.view(np.uint32)), (N, K, bi)
 
 
 @pytest.mark.parametrize("n_live", [1, 2, 4])
@@ -198,15 +213,15 @@ def test_pad_slots_do_not_leak():
     Xq = gpu_quantize_acts(X)
     bi = np.array([2, 9, 5], dtype=np.int32)
     clean = {p: gpu_matmul(Wq, Xq, bi, N, K, p) for p in (MFMA, DOT4)}
-    raw = Xq.view(16, -1)
+    q, d = slots_host(Xq, K)
     for s in range(16):
         if s in bi:
             continue
-        raw[s].copy_(torch.from_numpy(rng.integers(0, 256, raw.shape[1], dtype=np.uint8)))
-    import quantized_weight_streaming_q8_amd as q8
-    qv, dv = q8.split_act_slots(Xq, K)
-    dv[0].fill_(0x7c00)   # +inf
-    dv[1].fill_(0x7e00)   # NaN
+        q[s] = rng.integers(-128, 128, size=K).astype(np.int8)
+        d[s] = rng.integers(0, 1 << 16, size=K // 32).astype(np.uint16)
+    d[0] = 0x7c00  # +inf
+    d[1] = 0x7e00  # NaN
+    write_slots(Xq, K, q, d)
     for p in (MFMA, DOT4):
         assert np.array_equal(gpu_matmul(Wq, Xq, bi, N, K, p).view(np.uint32),
                               clean[p].view(np.uint32))
@@ -224,6 +239,28 @@ def test_bad_batch_index_gives_nan_row():
         Y = gpu_matmul(Wq, Xq, bi, N, K, p)
         assert np.all(np.isnan(Y[[1, 2, 4]]))
         assert within_tau(Y[[0, 3]], Yo, Ao)[0]
+
+
+def test_workspace_is_rearmed_by_every_call():
+    """A workspace used by many calls in a row (and by calls with different
+    live batches) keeps giving the plain entry point's bits, and is all zero
+    again after each call."""
+    import quantized_weight_streaming_q8_amd as q8
+    rng = np.random.default_rng(37)
+    N, K = 5120, 5120
+    assert q8.q8_matmul_workspace_bytes(N, K) > 0
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    X = rng.standard_normal((16, K), dtype=np.float32)
+    Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
+    ws = q8.zeroed_workspace(N, K)
+    nbytes_counters = -(-(-(-N // 16)) * 4 // 256) * 256
+    for rep in range(3):
+        for n in (16, 1, 5):
+            bi = rng.permutation(16)[:n].astype(np.int32)
+            Yp = gpu_matmul(Wq, Xq, bi, N, K)
+            Yw = gpu_matmul_ws(Wq, Xq, bi, N, K, ws)
+            assert np.array_equal(Yp.view(np.uint32), Yw.view(np.uint32)), (rep, n)
+            assert not ws[:nbytes_counters].any()
 
 
 def test_columns_equal_single_token_calls():
@@ -255,6 +292,8 @@ def test_qwen3_layer_every_live_batch():
     for idx, m in enumerate(w.matrices):
         W, X = wl.workload_inputs("qwen3_layer", idx)
         Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
+        import quantized_weight_streaming_q8_amd as q8
+        ws = q8.zeroed_workspace(m.N, m.K)
         rows = sample_rows(m.N, 96, seed=idx)
         qw, dw = oracle.quantize_rows(W[rows])
         qx, dx = oracle.quantize_rows(X)
@@ -265,6 +304,8 @@ def test_qwen3_layer_every_live_batch():
             Yo, Ao = oracle.matmul(qw, dw, qx, dx, bi)
             ok, worst = within_tau(Y[:, rows], Yo, Ao)
             assert ok, (m.name, n_live, worst)
+            Yw = gpu_matmul_ws(Wq, Xq, bi, m.N, m.K, ws)
+            assert np.array_equal(Y.view(np.uint32), Yw.view(np.uint32)), (m.name, n_live)
             if n_live in (1, 7, 16):
                 Yd = gpu_matmul(Wq, Xq, bi, m.N, m.K, DOT4)
                 assert np.array_equal(Y.view(np.uint32), Yd.view(np.uint32)), (m.name, n_live)
@@ -316,9 +357,13 @@ def test_large_dense_schedule(idx):
     Y = torch.empty((16, m.N), dtype=torch.float32, device="cuda")
     ref = torch.from_numpy(Y16).cuda()
     bad = torch.zeros((), dtype=torch.int64, device="cuda")
-    for bi in sched:
+    ws = q8.zeroed_workspace(m.N, m.K)
+    for i, bi in enumerate(sched):
         bi_d = to_dev(bi)
         n = bi.size
-        q8.q8_matmul_narrow(Wq, Xq, bi_d, n, m.N, m.K, Y)
+        if i % 2:  # alternate the two entry points; both must give the same bits
+            q8.q8_matmul_narrow_ws(Wq, Xq, bi_d, n, m.N, m.K, Y, ws)
+        else:
+            q8.q8_matmul_narrow(Wq, Xq, bi_d, n, m.N, m.K, Y)
         bad += (Y[:n].view(torch.int32) != ref[bi_d.long()].view(torch.int32)).sum()
     assert int(bad) == 0
