@@ -189,6 +189,52 @@ def time_graph_steps(layer: Layer, n_live: int, steps: int, warmup: int):
     return dt * 1e3 / steps, same
 
 
+def graph_avg_us(launch, launches: int, replays: int = 3) -> float:
+    """Average duration of one launch: `launches` back-to-back launches
+    (launch(c) for c in range(launches)) captured in one HIP graph, replayed
+    `replays` times between one pair of HIP events on the launch stream, so
+    that neither the host's launch rate nor the events' own cost shows."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in range(4):
+            launch(c)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in range(launches):
+            launch(c)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / (launches * replays)
+
+
+def kernel_avg_us(layer: Layer, i: int, n_live: int, launches: int) -> float:
+    """Average duration of one launch of matrix i's narrow matmul (the
+    workspace entry point the step uses), back to back over the rotated
+    weight copies."""
+    q8, m = layer.q8, layer.mats[i]
+    bi = layer.batch_index(n_live)
+    return graph_avg_us(lambda c: q8.q8_matmul_narrow_ws(
+        layer.packed[c % layer.copies][i], layer.Xq[i], bi, n_live, m.N, m.K,
+        layer.Y[i], layer.ws[i]), launches)
+
+
+def quantize_avg_us(layer: Layer, i: int, launches: int = 100) -> float:
+    """Average duration of one pre-quantize launch (16 rows of matrix i's K)."""
+    q8, m = layer.q8, layer.mats[i]
+    return graph_avg_us(lambda c: q8.q8_quantize_acts(layer.X[i], 16, m.K, layer.Xq[i]), launches)
+
+
 def copy_ceiling_gbs(nbytes: int = 1 << 30, reps: int = 20) -> float:
     """Read+write rate of a plain device-to-device copy (torch's copy
     kernel), for context."""
@@ -272,6 +318,85 @@ def measured_traffic(n_live: int):
     return None if per is None else int(per)
 
 
+# --------------------------------------------------- HBM traffic counters
+#
+# Two rocprofv3 counter passes over `bench.py --pmc-probe` (FETCH_SIZE, then
+# WRITE_SIZE) read the HBM traffic of the dominant matmul.  The same probe
+# runs a plain device copy of CAL_BYTES, whose true traffic is known (read
+# CAL_BYTES, write CAL_BYTES); each counter is scaled by known / counted on
+# that copy.  `bench.py --pmc-summarize FETCH_CSV WRITE_CSV` turns the two
+# counter_collection.csv files into the committed summary that the JSON
+# line's roofline.traffic reads back.
+
+CAL_BYTES = 256 << 20
+
+
+def pmc_probe(launches: int, n_live: int) -> None:
+    """The dominant matmul of the Layer workload, `launches` times over two
+    weight copies, then the calibration copy three times."""
+    import torch
+    import quantized_weight_streaming_q8_amd as q8
+    w = wl.WORKLOADS["qwen3_layer"]
+    i = [k for k, m in enumerate(w.matrices) if m.name == DOMINANT][0]
+    m = w.matrices[i]
+    W = torch.from_numpy(wl.weights(w.config, i, m.N, m.K)).cuda()
+    packed = [q8.empty_packed_weights(m.N, m.K) for _ in range(2)]
+    for P in packed:
+        q8.q8_pack_weights(W, m.N, m.K, P)
+    del W
+    X = torch.from_numpy(wl.activations(w.config, m.K, outliers=w.outliers)).cuda()
+    Xq = q8.empty_act_slots(m.K)
+    q8.q8_quantize_acts(X, 16, m.K, Xq)
+    Y = torch.empty((16, m.N), dtype=torch.float32, device="cuda")
+    ws = q8.zeroed_workspace(m.N, m.K)
+    bi = torch.from_numpy(wl.batch_index(w.config, n_live, random=w.random_batch_index)).cuda()
+    for c in range(launches):
+        q8.q8_matmul_narrow_ws(packed[c % 2], Xq, bi, n_live, m.N, m.K, Y, ws)
+    torch.cuda.synchronize()
+    a = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"pmc probe: {launches} launches of {m.name} at n_live={n_live}, 3 copies of {CAL_BYTES} B",
+          flush=True)
+
+
+def _counter_rows(path: str, counter: str):
+    import csv
+    with open(path) as f:
+        return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+
+
+def pmc_summarize(fetch_csv: str, write_csv: str, n_live: int, out: str) -> dict:
+    """Per-launch HBM bytes of the dominant matmul from the two counter
+    passes, each scaled by the calibration copy."""
+    res = {"kernel_source_hash": kernel_source_hash(), "n_live": n_live,
+           "calibration_copy_bytes": CAL_BYTES}
+    per = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path, name)
+        mm = [float(r["Counter_Value"]) for r in rows if "mm_mfma_kernel" in r["Kernel_Name"]]
+        last_mm = max(int(r["Dispatch_Id"]) for r in rows if "mm_mfma_kernel" in r["Kernel_Name"])
+        cal = [float(r["Counter_Value"]) for r in rows
+               if "copyBuffer" in r["Kernel_Name"] and int(r["Dispatch_Id"]) > last_mm]
+        if not mm or not cal:
+            raise SystemExit(f"{path}: no matmul or calibration dispatches for {name}")
+        scale = (CAL_BYTES / 1024.0) / float(np.median(cal))  # counters are in KiB
+        per[name] = {"matmul_KiB_per_dispatch_median": float(np.median(mm)),
+                     "calibration_KiB_median": float(np.median(cal)),
+                     "scale": scale,
+                     "bytes_per_launch": float(np.median(mm)) * 1024.0 * scale,
+                     "dispatches": len(mm)}
+    res["counters"] = per
+    res["traffic_bytes_per_launch"] = {
+        str(n_live): int(per["FETCH_SIZE"]["bytes_per_launch"] + per["WRITE_SIZE"]["bytes_per_launch"])}
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    return res
+
+
 # ------------------------------------------------------------------ main
 
 def main(argv=None) -> int:
@@ -288,7 +413,17 @@ def main(argv=None) -> int:
     ap.add_argument("--out", default=None, help="also write the JSON line here")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--pmc-probe", type=int, default=0, metavar="LAUNCHES",
+                    help="only launch the dominant matmul this many times and the "
+                         "calibration copy (for rocprofv3 --pmc)")
+    ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary from two counter_collection.csv files")
     args = ap.parse_args(argv)
+
+    if args.pmc_summarize:
+        path = os.path.join(PROFILE_DIR, "gate_up_matmul_qwen3_layer_pmc.json")
+        print(json.dumps(pmc_summarize(*args.pmc_summarize, args.n_live, path), indent=1))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
@@ -300,63 +435,72 @@ def main(argv=None) -> int:
 
     import torch
     torch.cuda.set_device(0)
+    if args.pmc_probe:
+        pmc_probe(args.pmc_probe, args.n_live)
+        return 0
     layer = Layer(args.workload)
     mats = layer.mats
     print(f"# {args.workload}: {len(mats)} matrices, {layer.packed_bytes / 1e6:.1f} MB packed, "
           f"{layer.copies} copies rotated", file=sys.stderr, flush=True)
 
-    ms_eager, kern = time_steps(layer, args.n_live, args.steps, args.warmup, with_events=True)
+    ms_eager, _ = time_steps(layer, args.n_live, args.steps, args.warmup, with_events=False)
     graph_ok = None
     ms = ms_eager
     if args.graph:
         ms_graph, graph_ok = time_graph_steps(layer, args.n_live, args.steps, args.warmup)
-        if graph_ok:
+        if graph_ok and ms_graph < ms_eager:
             ms = ms_graph
     nbytes = step_bytes(mats, args.n_live)
     gbs = nbytes / (ms * 1e-3) / 1e9
     print(f"# n_live={args.n_live}: {ms * 1e3:.1f} us/step ({'graph' if ms is not ms_eager else 'eager'}), "
           f"eager {ms_eager * 1e3:.1f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
+    # each kernel alone: back-to-back launches between one pair of events
+    launches = max(64, 4 * layer.copies)
     per_matrix = {}
+    kern_us = []
     for i, m in enumerate(mats):
-        k = np.array(kern[i])
+        us = kernel_avg_us(layer, i, args.n_live, launches)
+        kern_us.append(us)
         b = matmul_bytes(m.N, m.K, args.n_live)
         per_matrix[m.name] = {
-            "K": m.K, "N": m.N, "us": round(float(k.mean()) * 1e3, 2),
-            "us_p90": round(float(np.percentile(k, 90)) * 1e3, 2),
-            "GBps": round(b / (k.mean() * 1e-3) / 1e9, 1),
-            "frac_peak": round(b / (k.mean() * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "K": m.K, "N": m.N, "us": round(us, 2), "GBps": round(b / us / 1e3, 1),
+            "frac_peak": round(b / us / 1e3 / PEAK_HBM_GBS, 4),
+            "quantize_us": round(quantize_avg_us(layer, i), 2),
         }
+    mm_bytes = sum(matmul_bytes(m.N, m.K, args.n_live) for m in mats)
+    print(f"# matmuls alone: {sum(kern_us):.1f} us, {mm_bytes / sum(kern_us) / 1e3:.0f} GB/s; "
+          + ", ".join(f"{m.name} {u:.2f} us" for m, u in zip(mats, kern_us)), file=sys.stderr, flush=True)
 
     dom = [i for i, m in enumerate(mats) if m.name == DOMINANT]
     di = dom[0] if dom else int(np.argmax([m.N * m.K for m in mats]))
     dm = mats[di]
     dom_bytes = matmul_bytes(dm.N, dm.K, args.n_live)
-    dom_ms = float(np.mean(kern[di]))
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    dom_us = kern_us[di]
+    achieved = dom_bytes / dom_us / 1e3
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
         "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(args.n_live),
         "kernel": f"q8 narrow matmul, {dm.name} {dm.K}->{dm.N}, n_live={args.n_live}",
-        "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2),
+        "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 2),
     }
 
     sweep = {}
     if args.sweep_steps > 0:
         for n in range(1, 17):
-            ms_e, kn = time_steps(layer, n, args.sweep_steps, min(args.warmup, 20), with_events=True)
+            ms_e, _ = time_steps(layer, n, args.sweep_steps, min(args.warmup, 20), with_events=False)
             ms_n = ms_e
             if args.graph:
                 ms_g, ok = time_graph_steps(layer, n, args.sweep_steps, min(args.warmup, 20))
-                if ok:
+                if ok and ms_g < ms_e:
                     ms_n = ms_g
-            kmean = [float(np.mean(x)) for x in kn]
+            kn = [kernel_avg_us(layer, i, n, max(16, 2 * layer.copies)) for i in range(len(mats))]
             sweep[n] = {"ms_per_step": round(ms_n, 4), "ms_per_step_eager": round(ms_e, 4),
                         "GBps": round(step_bytes(mats, n) / (ms_n * 1e-3) / 1e9, 1),
-                        "kernel_us": round(sum(kmean) * 1e3, 2),
+                        "kernel_us": round(sum(kn), 2),
                         "kernel_GBps": round(sum(matmul_bytes(m.N, m.K, n) for m in mats)
-                                             / (sum(kmean) * 1e-3) / 1e9, 1)}
-            print(f"# sweep n_live={n}: {ms_n * 1e3:.1f} us/step, kernels {sum(kmean) * 1e3:.1f} us",
+                                             / sum(kn) / 1e3, 1)}
+            print(f"# sweep n_live={n}: {ms_n * 1e3:.1f} us/step, matmuls {sum(kn):.1f} us",
                   file=sys.stderr, flush=True)
     ratio = None
     if sweep:
@@ -379,12 +523,14 @@ def main(argv=None) -> int:
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "ms_per_step_eager": round(ms_eager, 5),
-        "timing": "hip graph replay per step (checked bit-identical to eager)" if ms is not ms_eager
-        else "eager launches",
+        "timing": ("hip graph replay per step (checked bit-identical to eager)" if ms is not ms_eager
+                   else "eager launches on one stream") + "; the faster of the two",
+        "ms_per_step_graph": round(ms_graph, 5) if args.graph else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 dot, fp32 accumulate",
+        "dtype": "i8",
+        "accumulate": "exact i32 per 32-value block, f32 across blocks",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations, 1% outlier channels x20)",
         "config": {
             "workload": f"{args.workload}: Qwen3-14B-shaped decode layer" if args.workload == "qwen3_layer"
@@ -397,6 +543,8 @@ def main(argv=None) -> int:
         },
         "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
         "step_bytes": nbytes,
+        "matmul_us": round(sum(kern_us), 2),
+        "matmul_GBps": round(mm_bytes / sum(kern_us) / 1e3, 1),
         "t16_over_t1": ratio,
         "per_matrix": per_matrix,
         "sweep": sweep,

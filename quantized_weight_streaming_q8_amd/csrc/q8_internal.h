@@ -133,7 +133,8 @@ hipError_t launch_quantize_acts(const float* X, int n_rows, const Shape& s,
 // Matmul tiling: chosen from (N, K) only, so that the fp32 summation order
 // of every output never depends on the live batch.
 struct Tiling {
-    int rg;           // row groups of 16 rows per wave (MFMA engine)
+    int rg;           // row groups of 16 rows per wave (MFMA engine, one workgroup per row block)
+    int rg_split;     // the same when the splits run as separate workgroups
     int splits;       // K splits (level 2 of the summation tree)
     int kw;           // wave slices per split (level 1)
     bool nt_weights;  // non-temporal loads for the weight stream

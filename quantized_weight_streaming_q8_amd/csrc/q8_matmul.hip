@@ -27,13 +27,14 @@
 // Two int8 dot engines compute S, with the same accumulation order, so their
 // results are bit-identical:
 //   * MFMA: one v_mfma_i32_16x16x32_i8 per (16 rows, block) dots the block
-//     against 16 token slots at once.  A = weights (row = lane & 15), B =
-//     activations (token = lane & 15), D[row][token] -> lane holds token
-//     lane & 15 for rows 4*(lane >> 4) + r, so a lane needs one token's
-//     activation scales and four consecutive rows' weight scales, each one
-//     small load per chunk.  The cost is the same for any n_live: the weight
-//     stream is what the kernel spends its time on.  A wave covers RG row
-//     groups, so each activation load feeds 16*RG rows.
+//     against all 16 activation slots at once.  A = weights (row = lane & 15),
+//     B = slots (slot = lane & 15), D[row][slot] -> lane holds slot lane & 15
+//     for rows 4*(lane >> 4) + r, so a lane needs one slot's activation
+//     scales and four consecutive rows' weight scales, each one small load
+//     per chunk.  The cost is the same for any n_live: the weight stream is
+//     what the kernel spends its time on.  Tokens take their slot's column
+//     when the outputs are stored.  A wave covers RG row groups, so each
+//     activation load feeds 16*RG rows.
 //   * DOT4: one output row per lane, v_dot4 over the row's 32 bytes against
 //     the token's block (wave-uniform, so it comes through scalar loads).  Its
 //     VALU work grows with n_live.
@@ -41,8 +42,7 @@
 // Token slots come from batch_index ("[feature] Enable Dynamic Batching",
 // section "Objective": batch_index selects rows of a fixed, fully sized
 // buffer).  The slot buffer has the packed layout of a 16-row matrix, so the
-// activation operand of one chunk for all 16 slots is 1 KB contiguous.  Lanes
-// of tokens t >= n_live read token 0's slot and their results are dropped; a
+// activation operand of one chunk for all 16 slots is 1 KB contiguous.  A
 // slot index outside [0,16) is never read through (slot 0 is read instead)
 // and its output row is written as NaN.
 
@@ -152,83 +152,79 @@ __device__ inline float tree_sum(const float* red, int E, int e, int S, int KW) 
 // MFMA engine
 // ------------------------------------------------------------------------
 
-// The MFMA engine streams its K-slice one chunk (2 blocks, 1 KB per row
-// group) at a time through a ring of D chunks: it dots the oldest chunk and
-// issues the load of the chunk D places ahead, so every wave keeps a small,
-// steady stream of requests in flight (the way a plain streaming read
-// reaches full bandwidth) instead of bursts of whole super-chunks.
+// The MFMA engine dots every chunk against all 16 activation slots, whatever
+// the live batch: one 16x16x32 MFMA costs the same for 1 or 16 columns, and
+// nothing in the streaming loop then depends on batch_index.  The tokens are
+// picked out of the slot columns only when the outputs are stored (token t
+// takes slot batch_index[t]'s column), which gives each token exactly the
+// arithmetic of its own slot.  A slot no token names is computed and
+// dropped; its values, whatever they are, never reach another column.
+//
+// Each wave streams its K-slice one chunk (2 blocks, 1 KB per row group) at a
+// time through a ring of D chunks: it dots the oldest chunk and issues the
+// loads of the chunk D places ahead, so every wave keeps a steady stream of
+// requests in flight.  A slice is a whole number of super-chunks (4 chunks),
+// so with D dividing 4 the ring needs no bounds tests: every load and every
+// wait is the same in every turn of the loop.
+
+typedef long v2i64 __attribute__((ext_vector_type(2)));
+
+__device__ inline v2i64 ld16_v2(const void* p) {
+    return *reinterpret_cast<const v2i64*>(p);
+}
+
+__device__ inline v2i64 ld16_v2_nt(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const v2i64*>(p));
+}
 
 // Operands of one chunk for RG row groups, as loaded.
 template <int RG>
 struct Chunk {
-    uint4 w[RG];       // weights: this lane's A operands of blocks 2c, 2c+1
+    v2i64 w[RG];       // weights: this lane's A operands of blocks 2c, 2c+1
     uint4 wd[RG];      // rows 4*tq .. 4*tq+3: binary16 scales of blocks 2c, 2c+1
-    uint4 aq;          // activations: B operands of blocks 2c, 2c+1
-    uint32_t dx;       // token lane & 15: binary16 scales of blocks 2c, 2c+1
+    v2i64 aq;          // slot lane & 15: B operands of blocks 2c, 2c+1
+    uint32_t dx;       // slot lane & 15: binary16 scales of blocks 2c, 2c+1
 };
 
-// Chunk cg (global chunk index along K) of the weight stream; independent of
-// the live batch, so it can be issued before batch_index has been read.
+// Chunk cg (global chunk index along K) for RG row groups: weights, their
+// scales, and the slot operands (1 KB contiguous for the wave).
 template <int RG, bool NTW>
-__device__ inline void load_chunk_w(Chunk<RG>& ch, int cg, const uint8_t* wrow,
-                                    const uint16_t* wdrow, int64_t g_stride_q,
-                                    int64_t g_stride_d) {
+__device__ inline void load_chunk(Chunk<RG>& ch, int cg, const uint8_t* wrow,
+                                  const uint16_t* wdrow, int64_t g_stride_q,
+                                  int64_t g_stride_d, const uint8_t* xa,
+                                  const uint16_t* xdp) {
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
         const uint8_t* p = wrow + rg * g_stride_q + (int64_t)cg * kChunkBytes;
-        ch.w[rg] = NTW ? ld16_nt(p) : ld16(p);
+        ch.w[rg] = NTW ? ld16_v2_nt(p) : ld16_v2(p);
         ch.wd[rg] = ld16(wdrow + rg * g_stride_d + (int64_t)cg * (kChunkDBytes / 2));
     }
-}
-
-template <int RG>
-__device__ inline void load_chunk_a(Chunk<RG>& ch, int cg, const uint8_t* xa, const uint16_t* xdp) {
-    ch.aq = ld16(xa + (int64_t)cg * kChunkBytes);
+    ch.aq = ld16_v2(xa + (int64_t)cg * kChunkBytes);
     ch.dx = *reinterpret_cast<const uint32_t*>(xdp + (int64_t)cg * (kChunkDBytes / 2));
 }
 
-// Dot chunk cg and accumulate: acc[rg][r] is row 4*tq + r of row group rg
-// for token lane & 15.
+// Dot one chunk and accumulate: acc[rg][r] is row 4*tq + r of row group rg
+// for slot lane & 15.  Blocks past K (the padding of the last super-chunk)
+// hold zero codes and zero scales on both sides: their term is
+// fma(0, +0, acc), which returns acc unchanged (acc starts at +0 and no term
+// can make it -0), so they need no test.
 template <int RG>
-__device__ inline void mfma_chunk(const Chunk<RG>& ch, int cg, int KB, float acc[RG][4]) {
-    const int b0 = 2 * cg, b1 = 2 * cg + 1;
-    const long xa0 = (long)((uint64_t)ch.aq.x | ((uint64_t)ch.aq.y << 32));
-    const long xa1 = (long)((uint64_t)ch.aq.z | ((uint64_t)ch.aq.w << 32));
+__device__ inline void mfma_chunk(const Chunk<RG>& ch, float acc[RG][4]) {
     const _Float16 dx0 = half_bits(ch.dx, 0), dx1 = half_bits(ch.dx, 1);
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-        const long w0 = (long)((uint64_t)ch.w[rg].x | ((uint64_t)ch.w[rg].y << 32));
-        const long w1 = (long)((uint64_t)ch.w[rg].z | ((uint64_t)ch.w[rg].w << 32));
         const v4i zero = {0, 0, 0, 0};
-        const v4i S0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(w0, xa0, zero, 0, 0, 0);
-        const v4i S1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(w1, xa1, zero, 0, 0, 0);
+        const v4i S0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(ch.w[rg].x, ch.aq.x, zero, 0, 0, 0);
+        const v4i S1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(ch.w[rg].y, ch.aq.y, zero, 0, 0, 0);
         // wd[rg]: row 4*tq + r has its block-2c scale in half 2r, block 2c+1 in 2r+1
-        if (b0 < KB) {  // blocks past K are padding
-            acc[rg][0] = term_fma(S0[0], half_bits(ch.wd[rg].x, 0), dx0, acc[rg][0]);
-            acc[rg][1] = term_fma(S0[1], half_bits(ch.wd[rg].y, 0), dx0, acc[rg][1]);
-            acc[rg][2] = term_fma(S0[2], half_bits(ch.wd[rg].z, 0), dx0, acc[rg][2]);
-            acc[rg][3] = term_fma(S0[3], half_bits(ch.wd[rg].w, 0), dx0, acc[rg][3]);
-        }
-        if (b1 < KB) {
-            acc[rg][0] = term_fma(S1[0], half_bits(ch.wd[rg].x, 1), dx1, acc[rg][0]);
-            acc[rg][1] = term_fma(S1[1], half_bits(ch.wd[rg].y, 1), dx1, acc[rg][1]);
-            acc[rg][2] = term_fma(S1[2], half_bits(ch.wd[rg].z, 1), dx1, acc[rg][2]);
-            acc[rg][3] = term_fma(S1[3], half_bits(ch.wd[rg].w, 1), dx1, acc[rg][3]);
-        }
-    }
-}
-
-typedef __attribute__((address_space(4))) const int ci32;
-
-// Slot of every token lane, read through the scalar cache (a separate
-// counter from the vector loads, so waiting for it never waits for the
-// weight stream).  Tokens past n_live take token 0's slot; an index outside
-// [0,16) reads slot 0 (its output row is written as NaN).
-__device__ inline void token_slots(const MmArgs& a, int sl[16]) {
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        const int s = ((ci32*)a.bidx)[t < a.n_live ? t : 0];
-        sl[t] = (s >= 0 && s < kMaxSlots) ? s : 0;
+        acc[rg][0] = term_fma(S0[0], half_bits(ch.wd[rg].x, 0), dx0, acc[rg][0]);
+        acc[rg][1] = term_fma(S0[1], half_bits(ch.wd[rg].y, 0), dx0, acc[rg][1]);
+        acc[rg][2] = term_fma(S0[2], half_bits(ch.wd[rg].z, 0), dx0, acc[rg][2]);
+        acc[rg][3] = term_fma(S0[3], half_bits(ch.wd[rg].w, 0), dx0, acc[rg][3]);
+        acc[rg][0] = term_fma(S1[0], half_bits(ch.wd[rg].x, 1), dx1, acc[rg][0]);
+        acc[rg][1] = term_fma(S1[1], half_bits(ch.wd[rg].y, 1), dx1, acc[rg][1]);
+        acc[rg][2] = term_fma(S1[2], half_bits(ch.wd[rg].z, 1), dx1, acc[rg][2]);
+        acc[rg][3] = term_fma(S1[3], half_bits(ch.wd[rg].w, 1), dx1, acc[rg][3]);
     }
 }
 
@@ -242,14 +238,43 @@ __device__ inline void coherent_store(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Output element o of a tile, numbered token-major so that 16 consecutive
+// threads store 16 consecutive rows of one token (64 contiguous bytes):
+// o = (t*RG + rg)*16 + j is token t, row (gbase + rg)*16 + j.  The waves
+// wrote row j = 4*tq + r of slot s at tile element rg*256 + r*64 + tq*16 + s.
+struct TileOut {
+    int t;        // token
+    int e;        // tile element of the token's slot column
+    int64_t n;    // output row
+    bool store;   // inside the matrix, a live token, a row group of this block
+    bool bad;     // the token's slot index is outside [0, 16)
+};
+
+template <int RG>
+__device__ inline TileOut tile_out(const MmArgs& a, const int* tok_slot, int o,
+                                   int64_t gbase, int gskip) {
+    TileOut r;
+    r.t = o / (RG * 16);
+    const int rg = (o >> 4) & (RG - 1);
+    const int j = o & 15;
+    r.n = (gbase + rg) * kRowsPerGroup + j;
+    r.store = rg >= gskip && r.t < a.n_live && r.n < a.N;
+    const int s = tok_slot[r.t];
+    r.bad = s < 0 || s >= kMaxSlots;
+    r.e = rg * 256 + (j & 3) * 64 + (j >> 2) * 16 + (r.bad ? 0 : s);
+    return r;
+}
+
 // One workgroup per row block (plain: all S*KW waves) or per (row block,
 // split) (SPLIT: KW waves).  LDS: the wave partials red fp32 [waves][RG*256].
 template <int RG, int D, bool NTW, bool SPLIT>
 __global__ void __launch_bounds__(512)
 mm_mfma_kernel(MmArgs a) {
+    static_assert(D == 1 || D == 2 || D == 4, "the ring depth must divide a super-chunk");
+    static_assert(RG == 1 || RG == 2, "row groups per wave");
     extern __shared__ __align__(16) float red[];
     __shared__ int last_flag;
-    constexpr int E = RG * 256;  // output tile: RG row groups x 16 rows x 16 tokens
+    constexpr int E = RG * 256;  // output tile: RG row groups x 16 rows x 16 slots
     const int lane = threadIdx.x & 63;
     const int tq = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -258,7 +283,7 @@ mm_mfma_kernel(MmArgs a) {
     const int split = SPLIT ? (int)(blockIdx.x % a.S) : w / a.KW;
     int sc0, sc1;
     slice_range(a.NSC, a.S, a.KW, split, SPLIT ? w : w % a.KW, sc0, sc1);
-    const int c_lo = 4 * sc0, c_hi = 4 * sc1;  // this wave's chunks
+    const int c_lo = 4 * sc0, c_hi = 4 * sc1;  // this wave's chunks (>= 4)
 
     // weights: RG consecutive row groups; the last row block may start
     // earlier (gbase < g0) so that every load stays inside the buffer, and
@@ -269,6 +294,8 @@ mm_mfma_kernel(MmArgs a) {
     const int64_t gd = (int64_t)a.NSC * 4 * (kChunkDBytes / 2);  // halves per row group
     const uint8_t* wrow = a.wq + gbase * gq + lane * 16;
     const uint16_t* wdrow = a.wd + gbase * gd + tq * 8;
+    const uint8_t* xa = a.xq + lane * 16;
+    const uint16_t* xdp = a.xd + (lane & 15) * 2;
     const int gskip = (int)(g0 - gbase);
 
     float acc[RG][4];
@@ -277,70 +304,51 @@ mm_mfma_kernel(MmArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[rg][r] = 0.0f;
 
-    // the first weights go out before anything waits for batch_index
+    // the live tokens' slots, for the output gather: read now, so that the
+    // load's latency hides behind the weight stream
+    __shared__ int tok_slot[16];
+    int my_slot = 0;
+    if (threadIdx.x < 16 && (int)threadIdx.x < a.n_live) my_slot = a.bidx[threadIdx.x];
+
     Chunk<RG> ring[D];
 #pragma unroll
-    for (int i = 0; i < D; ++i)
-        if (c_lo + i < c_hi) load_chunk_w<RG, NTW>(ring[i], c_lo + i, wrow, wdrow, gq, gd);
-
-    int sl[16];
-    token_slots(a, sl);
-    // this lane's token: B operand at k-slot tq, and its scales
-    int sa = sl[0];
-#pragma unroll
-    for (int t = 1; t < 16; ++t) sa = (lane & 15) == t ? sl[t] : sa;
-    const uint8_t* xa = a.xq + (tq * 16 + sa) * 16;
-    const uint16_t* xdp = a.xd + sa * 2;
-#pragma unroll
-    for (int i = 0; i < D; ++i)
-        if (c_lo + i < c_hi) load_chunk_a<RG>(ring[i], c_lo + i, xa, xdp);
-
-    // dot the oldest chunk, load the one D ahead
+    for (int i = 0; i < D; ++i) load_chunk<RG, NTW>(ring[i], c_lo + i, wrow, wdrow, gq, gd, xa, xdp);
     int c = c_lo;
-    for (; c + 2 * D <= c_hi; c += D) {
+    for (; c + D < c_hi; c += D) {
 #pragma unroll
         for (int i = 0; i < D; ++i) {
-            mfma_chunk<RG>(ring[i], c + i, a.KB, acc);
-            load_chunk_w<RG, NTW>(ring[i], c + i + D, wrow, wdrow, gq, gd);
-            load_chunk_a<RG>(ring[i], c + i + D, xa, xdp);
+            mfma_chunk<RG>(ring[i], acc);
+            load_chunk<RG, NTW>(ring[i], c + D + i, wrow, wdrow, gq, gd, xa, xdp);
+            // keep each chunk's loads right after its dot: left alone, the
+            // scheduler sinks all D chunks' loads to the end of the turn,
+            // and every turn then waits a full memory latency
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
-    for (int i = 0; i < D; ++i) {  // fewer than 2D chunks left, D in the ring
-        if (c + i < c_hi) {
-            mfma_chunk<RG>(ring[i], c + i, a.KB, acc);
-            if (c + i + D < c_hi) {
-                load_chunk_w<RG, NTW>(ring[i], c + i + D, wrow, wdrow, gq, gd);
-                load_chunk_a<RG>(ring[i], c + i + D, xa, xdp);
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < D; ++i)
-        if (c + D + i < c_hi) mfma_chunk<RG>(ring[i], c + D + i, a.KB, acc);
+    for (int i = 0; i < D; ++i) mfma_chunk<RG>(ring[i], acc);
 
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
         for (int r = 0; r < 4; ++r) red[(w * RG + rg) * 256 + r * 64 + lane] = acc[rg][r];
+    if (threadIdx.x < 16) tok_slot[threadIdx.x] = my_slot;
     __syncthreads();
 
     const int nthreads = nwaves * 64;
     if (!SPLIT) {
-        for (int e = threadIdx.x; e < E; e += nthreads) {
-            const float y = tree_sum(red, E, e, a.S, a.KW);
-            const int rg = e >> 8, r = (e >> 6) & 3, ln = e & 63;
-            const int t = ln & 15;
-            const int64_t n = (gbase + rg) * kRowsPerGroup + 4 * (ln >> 4) + r;
-            if (rg >= gskip && t < a.n_live && n < a.N)
-                a.Y[(int64_t)t * a.N + n] = slot_bad(a.bidx, t) ? __builtin_nanf("") : y;
+        for (int o = threadIdx.x; o < E; o += nthreads) {
+            const TileOut to = tile_out<RG>(a, tok_slot, o, gbase, gskip);
+            if (to.store)
+                a.Y[(int64_t)to.t * a.N + to.n] =
+                    to.bad ? __builtin_nanf("") : tree_sum(red, E, to.e, a.S, a.KW);
         }
         return;
     }
-    // level 1 of this split, published in the workspace.  The partials are
-    // written with device-coherent stores and the wait below makes them
-    // complete before the counter moves, so no cache has to be flushed; the
-    // last split reads them back with device-coherent loads.
+    // level 1 of this split, every slot column, published in the workspace.
+    // The partials are written with device-coherent stores and the wait below
+    // makes them complete before the counter moves, so no cache has to be
+    // flushed; the last split reads them back with device-coherent loads.
     float* mine = a.part + ((int64_t)split * a.n_rb + rb) * E;
     for (int e = threadIdx.x; e < E; e += nthreads) coherent_store(mine + e, split_sum(red, E, e, 0, a.KW));
     // every thread waits for its own stores to complete before the barrier,
@@ -355,28 +363,27 @@ mm_mfma_kernel(MmArgs a) {
     __syncthreads();
     if (!last_flag) return;
     // the last split to arrive: level 2 in split order, then rearm the counter
-    for (int e = threadIdx.x; e < E; e += nthreads) {
-        float y = coherent_load(a.part + (int64_t)rb * E + e);
-        for (int s = 1; s < a.S; ++s) y += coherent_load(a.part + ((int64_t)s * a.n_rb + rb) * E + e);
-        const int rg = e >> 8, r = (e >> 6) & 3, ln = e & 63;
-        const int t = ln & 15;
-        const int64_t n = (gbase + rg) * kRowsPerGroup + 4 * (ln >> 4) + r;
-        if (rg >= gskip && t < a.n_live && n < a.N)
-            a.Y[(int64_t)t * a.N + n] = slot_bad(a.bidx, t) ? __builtin_nanf("") : y;
+    for (int o = threadIdx.x; o < E; o += nthreads) {
+        const TileOut to = tile_out<RG>(a, tok_slot, o, gbase, gskip);
+        if (!to.store) continue;
+        float y = coherent_load(a.part + (int64_t)rb * E + to.e);
+        for (int s = 1; s < a.S; ++s) y += coherent_load(a.part + ((int64_t)s * a.n_rb + rb) * E + to.e);
+        a.Y[(int64_t)to.t * a.N + to.n] = to.bad ? __builtin_nanf("") : y;
     }
     if (threadIdx.x == 0) __hip_atomic_store(a.counters + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+int mfma_waves(const MmArgs& a, bool split) { return split ? a.KW : a.S * a.KW; }
+
 size_t mfma_lds_bytes(const MmArgs& a, int rg, bool split) {
-    const int waves = split ? a.KW : a.S * a.KW;
-    return (size_t)waves * rg * 256 * sizeof(float);
+    return (size_t)mfma_waves(a, split) * rg * 256 * sizeof(float);
 }
 
 int mfma_max_waves(int) { return 8; }  // 512 threads: 256 VGPRs per lane
 
 template <int RG, int D, bool NTW, bool SPLIT>
 hipError_t launch_mfma(const MmArgs& a, hipStream_t st) {
-    const int waves = SPLIT ? a.KW : a.S * a.KW;
+    const int waves = mfma_waves(a, SPLIT);
     const size_t lds = mfma_lds_bytes(a, RG, SPLIT);
     if (lds > kMaxLds || waves > mfma_max_waves(RG) || a.G < RG) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)(SPLIT ? (int64_t)a.n_rb * a.S : a.n_rb);
@@ -497,26 +504,33 @@ hipError_t launch_dot4(const MmArgs& a, hipStream_t st) {
 Tiling choose_tiling(const Shape& s) {
     // Rules measured on MI355X over the model-shaped matrices (K 5120..18432,
     // N 5120..151936):
-    //  * two row groups per wave (32 rows per activation load) once there are
-    //    enough row groups to fill the machine, else one;
-    //  * split K across workgroups until there are >= 4 workgroups per CU
-    //    (256 CUs), each split keeping >= 2 super-chunks;
-    //  * wave slices per split for about 4096 waves in the grid, at most 8
-    //    waves per workgroup and >= 1 super-chunk per wave.
+    //  * two row groups per wave (each activation load feeds 32 rows);
+    //  * 4 waves per row block while there are fewer than 512 row blocks
+    //    (up to ~8k rows), else 8: enough waves in the grid to keep ~5 MB of
+    //    weights in flight, few enough that a row block's waves finish
+    //    together;
+    //  * long rows (K >= 8192) are cut into 4 splits of one wave each, which
+    //    the workspace entry point runs as separate single-row-group
+    //    workgroups (more of them than there are CUs); shorter rows are one
+    //    split of 4 or 8 wave slices inside one workgroup;
+    //  * never more wave slices than super-chunks.
     Tiling t;
-    t.rg = s.G >= 1024 ? 2 : 1;
+    t.rg = s.G >= 2 ? 2 : 1;
     const int64_t n_rb = (s.G + t.rg - 1) / t.rg;
-    t.splits = 1;
-    while (t.splits < 8 && n_rb * t.splits < 1024 && s.NSC >= 4 * t.splits) t.splits *= 2;
-    const int max_waves = 8;  // 512-thread workgroups
-    int64_t kw = (4096 + n_rb * t.splits - 1) / (n_rb * t.splits);
-    kw = std::min<int64_t>(kw, max_waves / t.splits);
-    kw = std::min<int64_t>(kw, s.NSC / t.splits);
-    t.kw = (int)std::max<int64_t>(kw, 1);
+    const int P = n_rb < 512 ? 4 : 8;
+    if (s.NSC >= 32) {
+        t.splits = P;
+        t.kw = 1;
+        t.rg_split = 1;
+    } else {
+        t.splits = 1;
+        t.kw = (int)std::min<int64_t>(P, s.NSC);
+        t.rg_split = t.rg;
+    }
     t.nt_weights = true;
 #ifdef Q8_TUNING
     // measurement builds only: override the tiling from the environment
-    if (const char* e = getenv("Q8_RG")) t.rg = atoi(e) == 2 ? 2 : 1;
+    if (const char* e = getenv("Q8_RG")) t.rg = t.rg_split = atoi(e) == 2 ? 2 : 1;
     if (const char* e = getenv("Q8_S")) t.splits = std::max(1, atoi(e));
     if (const char* e = getenv("Q8_KW")) t.kw = std::max(1, atoi(e));
     if (const char* e = getenv("Q8_NTW")) t.nt_weights = atoi(e) != 0;
@@ -526,11 +540,14 @@ Tiling choose_tiling(const Shape& s) {
 
 // Row groups per wave actually launched (a matrix with fewer row groups than
 // asked for runs one per wave).
-int launch_rg(const Shape& s, const Tiling& t) { return s.G >= t.rg ? t.rg : 1; }
+int launch_rg(const Shape& s, const Tiling& t, bool split) {
+    const int rg = split ? t.rg_split : t.rg;
+    return s.G >= rg ? rg : 1;
+}
 
 size_t workspace_bytes(const Shape& s, const Tiling& t) {
     if (t.splits <= 1) return 0;
-    const int rg = launch_rg(s, t);
+    const int rg = launch_rg(s, t, true);
     const int64_t n_rb = (s.G + rg - 1) / rg;
     const int64_t counters = align_up(n_rb * 4, 256);
     return (size_t)(counters + (int64_t)t.splits * n_rb * rg * 256 * 4);
@@ -556,9 +573,9 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
     a.KW = t.kw;
     if (a.S * a.KW > a.NSC) return hipErrorInvalidValue;
     if (e == Engine::kDot4) return launch_dot4(a, st);
-    const int rg = launch_rg(s, t);
-    a.n_rb = (int)((s.G + rg - 1) / rg);
     const bool split = workspace != nullptr && t.splits > 1;
+    const int rg = launch_rg(s, t, split);
+    a.n_rb = (int)((s.G + rg - 1) / rg);
     a.counters = nullptr;
     a.part = nullptr;
     if (split) {

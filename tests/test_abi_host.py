@@ -138,9 +138,13 @@ def test_other_entry_points_reject_invalid_arguments(q8):
 
 
 def test_workspace_sizes(q8):
-    # small-N shapes are split across workgroups and need a workspace; the
-    # 151936-row head is not split
-    assert q8.q8_matmul_workspace_bytes(5120, 5120) > 0
+    # long rows (K >= 8192) are split across workgroups and need a workspace:
+    # a counter per row group (256-byte aligned) and 4 partial tiles of
+    # 16 x 16 fp32 per row group; shorter rows are not split
+    G = 5120 // 16
+    assert q8.q8_matmul_workspace_bytes(5120, 17408) == -(-G * 4 // 256) * 256 + 4 * G * 1024
+    assert q8.q8_matmul_workspace_bytes(7168, 18432) > 0
+    assert q8.q8_matmul_workspace_bytes(5120, 5120) == 0
     assert q8.q8_matmul_workspace_bytes(151936, 5120) == 0
     assert q8.q8_matmul_workspace_bytes(0, 5120) == 0
     assert q8.q8_matmul_workspace_bytes(16, 32) == 0  # one super-chunk: no split
@@ -149,11 +153,12 @@ def test_workspace_sizes(q8):
 def test_ws_entry_point_rejects_a_missing_or_small_workspace(q8):
     lib = q8.library()
     bad = q8.Q8_ERR_INVALID_ARG
-    need = q8.q8_matmul_workspace_bytes(5120, 5120)
-    assert lib.q8_matmul_narrow_ws(P, P, P, 4, 5120, 5120, P, None, need, None) == bad
-    assert lib.q8_matmul_narrow_ws(P, P, P, 4, 5120, 5120, P, P, need - 1, None) == bad
-    assert lib.q8_matmul_narrow_ws(P, P, P, 4, 5120, 5120, P, P + 16, need, None) == bad
-    assert lib.q8_matmul_narrow_ws(P, P, P, 0, 5120, 5120, P, P, need, None) == bad
+    need = q8.q8_matmul_workspace_bytes(5120, 17408)
+    assert need > 0
+    assert lib.q8_matmul_narrow_ws(P, P, P, 4, 5120, 17408, P, None, need, None) == bad
+    assert lib.q8_matmul_narrow_ws(P, P, P, 4, 5120, 17408, P, P, need - 1, None) == bad
+    assert lib.q8_matmul_narrow_ws(P, P, P, 4, 5120, 17408, P, P + 16, need, None) == bad
+    assert lib.q8_matmul_narrow_ws(P, P, P, 0, 5120, 17408, P, P, need, None) == bad
 
 
 def test_binding_raises_on_rejected_call(q8):

@@ -130,7 +130,7 @@ def _oracle_y(W, X, bi, rows=None):
 
 @pytest.mark.parametrize("N,K", [(1, 32), (17, 288), (15, 2080), (100, 800),
                                  (16, 256), (33, 4128), (768, 768), (40, 17408),
-                                 (1000, 5120), (5120, 2080)])
+                                 (17, 8224), (100, 9024), (1000, 5120), (5120, 2080)])
 def test_matmul_ragged_shapes(N, K):
     rng = np.random.default_rng(N + K)
     W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
@@ -247,7 +247,7 @@ def test_workspace_is_rearmed_by_every_call():
     again after each call."""
     import quantized_weight_streaming_q8_amd as q8
     rng = np.random.default_rng(37)
-    N, K = 5120, 5120
+    N, K = 5120, 17408  # long rows: the workspace entry point splits K across workgroups
     assert q8.q8_matmul_workspace_bytes(N, K) > 0
     W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
     X = rng.standard_normal((16, K), dtype=np.float32)
