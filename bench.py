@@ -318,6 +318,31 @@ def measured_traffic(n_live: int):
     return None if per is None else int(per)
 
 
+# ------------------------------------------------------- engine A/B
+
+def engine_ab(layer: Layer, n_values, launches: int) -> dict:
+    """Both int8 dot engines (MFMA tiles against all 16 slots; v_dot4 with
+    one row per lane and the live tokens' blocks through scalar loads) on
+    every matrix of the workload, plain entry point, per live batch: the
+    evidence for the default engine."""
+    q8 = layer.q8
+    out = {}
+    for i, m in enumerate(layer.mats):
+        for n in n_values:
+            bi = layer.batch_index(n)
+            rec = {}
+            for name, path in (("mfma", q8.Q8_PATH_MFMA), ("dot4", q8.Q8_PATH_DOT4)):
+                us = graph_avg_us(lambda c: q8.q8_matmul_narrow_path(
+                    layer.packed[c % layer.copies][i], layer.Xq[i], bi, n, m.N, m.K,
+                    layer.Y[i], path=path), launches)
+                rec[name] = {"us": round(us, 2),
+                             "GBps": round(matmul_bytes(m.N, m.K, n) / us / 1e3, 1)}
+            out[f"{m.name} n_live={n}"] = rec
+            print(f"# {m.name} n_live={n}: mfma {rec['mfma']['us']} us, dot4 {rec['dot4']['us']} us",
+                  file=sys.stderr, flush=True)
+    return out
+
+
 # --------------------------------------------------- HBM traffic counters
 #
 # Two rocprofv3 counter passes over `bench.py --pmc-probe` (FETCH_SIZE, then
@@ -418,6 +443,8 @@ def main(argv=None) -> int:
                          "calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two counter_collection.csv files")
+    ap.add_argument("--engine-ab", action="store_true",
+                    help="only time both dot engines on every matrix at n_live 1, 2, 4, 8, 16")
     args = ap.parse_args(argv)
 
     if args.pmc_summarize:
@@ -440,6 +467,14 @@ def main(argv=None) -> int:
         return 0
     layer = Layer(args.workload)
     mats = layer.mats
+    if args.engine_ab:
+        res = engine_ab(layer, (1, 2, 4, 8, 16), max(16, 2 * layer.copies))
+        text = json.dumps({"engine_ab": res, "workload": args.workload})
+        print(text, flush=True)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text + "\n")
+        return 0
     print(f"# {args.workload}: {len(mats)} matrices, {layer.packed_bytes / 1e6:.1f} MB packed, "
           f"{layer.copies} copies rotated", file=sys.stderr, flush=True)
 
