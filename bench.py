@@ -318,6 +318,39 @@ def measured_traffic(n_live: int):
     return None if per is None else int(per)
 
 
+# ------------------------------------------------- multi-token columns
+
+def multi_columns(layer: Layer, widths, launches: int) -> dict:
+    """The multi-column matmul (q8_matmul_multi) on every matrix of the
+    workload with n columns (n slots, all live, seeded random batch_index),
+    e.g. n_seq sequences x (k+1) speculative tokens: kernel time per launch,
+    algorithmic GB/s, and columns per microsecond."""
+    import torch
+    q8 = layer.q8
+    w = layer.w
+    out = {}
+    for n in widths:
+        rec = {}
+        bi = torch.from_numpy(wl.batch_index(w.config, n, random=True, n_slots=n)).cuda()
+        for i, m in enumerate(layer.mats):
+            X = torch.from_numpy(wl.activations(w.config, m.K, n_slots=n, outliers=w.outliers)).cuda()
+            Xq = q8.empty_act_slots(m.K, n_slots=n)
+            q8.q8_quantize_acts_n(X, n, m.K, Xq, n)
+            Y = torch.empty((n, m.N), dtype=torch.float32, device="cuda")
+            us = graph_avg_us(lambda c: q8.q8_matmul_multi(
+                layer.packed[c % layer.copies][i], Xq, n, bi, n, m.N, m.K, Y), launches)
+            rec[m.name] = {"us": round(us, 2), "GBps": round(matmul_bytes(m.N, m.K, n) / us / 1e3, 1)}
+            del X, Xq, Y
+        tot = sum(r["us"] for r in rec.values())
+        rec["all"] = {"us": round(tot, 2),
+                      "GBps": round(sum(matmul_bytes(m.N, m.K, n) for m in layer.mats) / tot / 1e3, 1),
+                      "columns_per_us": round(n / tot, 3)}
+        out[str(n)] = rec
+        print(f"# {n} columns: matmuls {tot:.1f} us, {rec['all']['GBps']} GB/s", file=sys.stderr,
+              flush=True)
+    return out
+
+
 # ------------------------------------------------------- engine A/B
 
 def engine_ab(layer: Layer, n_values, launches: int) -> dict:
@@ -443,6 +476,8 @@ def main(argv=None) -> int:
                          "calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two counter_collection.csv files")
+    ap.add_argument("--no-multi", dest="multi", action="store_false",
+                    help="skip the 16..64-column multi-token measurement")
     ap.add_argument("--engine-ab", action="store_true",
                     help="only time both dot engines on every matrix at n_live 1, 2, 4, 8, 16")
     args = ap.parse_args(argv)
@@ -546,6 +581,8 @@ def main(argv=None) -> int:
             rec["kernel_t_over_t1"] = round(rec["kernel_us"] / sweep[1]["kernel_us"], 4)
         ratio = sweep[16]["t_over_t1"]
 
+    multi = multi_columns(layer, (16, 32, 48, 64), max(16, 4 * layer.copies)) \
+        if args.multi else None
     copy_gbs = copy_ceiling_gbs()
     cpu = cpu_baseline(args.workload, args.n_live, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
@@ -584,6 +621,7 @@ def main(argv=None) -> int:
         "per_matrix": per_matrix,
         "sweep": sweep,
         "roofline": roofline,
+        "multi_columns": multi,
         "copy_ceiling_GBps": round(copy_gbs, 1),
         "cpu_baseline": cpu,
     }

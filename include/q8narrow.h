@@ -52,7 +52,8 @@ extern "C" {
 #endif
 
 #define Q8_BLOCK 32     /* values per q8_0 block */
-#define Q8_MAX_SLOTS 16 /* activation slots in the padded buffer */
+#define Q8_MAX_SLOTS 16   /* activation slots in the padded buffer */
+#define Q8_MAX_COLUMNS 64 /* slots of a multi-column buffer (q8_matmul_multi) */
 
 typedef enum q8_status {
     Q8_OK = 0,
@@ -165,6 +166,37 @@ q8_status q8_matmul_narrow_ws(const void* Wq, const void* Xq,
                               const int32_t* batch_index, int n_live,
                               int64_t N, int64_t K, float* Y, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------- multi-token columns */
+
+/* Several tokens per sequence in one step: "[feature] Enable Dynamic
+ * Batching", section "Assumptions and limitations" (dynamic batching
+ * combined with multi-spec speculative decoding: batch on one axis, the
+ * speculative length on the other, e.g. b=2, k=3 -> input_ids (2, 4)).  With
+ * n_seq sequences of k+1 tokens each, a weight block meets n_seq*(k+1)
+ * activation columns, up to Q8_MAX_COLUMNS here, and is still read from
+ * memory once.
+ *
+ * A multi-column slot buffer holds n_slots = 16, 32, 48 or 64 slots in the
+ * packed layout of an n_slots x K matrix (with n_slots = 16 it is exactly
+ * the q8_act_buffer_bytes buffer).  Returns its size in bytes, 0 if K or
+ * n_slots is invalid. */
+size_t q8_act_buffer_bytes_n(int64_t K, int n_slots);
+
+/* q8_quantize_acts for an n_slots buffer: rows X [n_rows][K] go to slots
+ * 0..n_rows-1; the others are left untouched.  1 <= n_rows <= n_slots. */
+q8_status q8_quantize_acts_n(const float* X, int n_rows, int64_t K, void* Xq,
+                             int n_slots, hipStream_t stream);
+
+/* q8_matmul_narrow over an n_slots buffer: Y [n_live][N], token t uses slot
+ * batch_index[t] in [0, n_slots); 1 <= n_live <= n_slots.  The summation
+ * tree is the one of q8_matmul_narrow (it depends on (N, K) only), so a
+ * column is bit-identical to q8_matmul_narrow's for the same slot contents,
+ * and to this call with n_live = 1.  A batch_index entry outside
+ * [0, n_slots) gives a NaN row. */
+q8_status q8_matmul_multi(const void* Wq, const void* Xq, int n_slots,
+                          const int32_t* batch_index, int n_live, int64_t N,
+                          int64_t K, float* Y, hipStream_t stream);
 
 /* ---------------------------------------------------------------- misc */
 

@@ -21,6 +21,7 @@ LIB_PATH = _build.LIB_PATH
 
 Q8_BLOCK = 32
 Q8_MAX_SLOTS = 16
+Q8_MAX_COLUMNS = 64
 
 Q8_OK = 0
 Q8_ERR_INVALID_ARG = 1
@@ -44,6 +45,9 @@ _SIGNATURES = {
     "q8_matmul_narrow_path": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp, _i32], _i32),
     "q8_matmul_workspace_bytes": ([_i64, _i64], ctypes.c_size_t),
     "q8_matmul_narrow_ws": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp], _i32),
+    "q8_act_buffer_bytes_n": ([_i64, _i32], ctypes.c_size_t),
+    "q8_quantize_acts_n": ([_vp, _i32, _i64, _vp, _i32, _vp], _i32),
+    "q8_matmul_multi": ([_vp, _vp, _i32, _vp, _i32, _i64, _i64, _vp, _vp], _i32),
     "q8_device_supported": ([], _i32),
     "q8_status_str": ([_i32], ctypes.c_char_p),
 }
@@ -167,6 +171,21 @@ def q8_matmul_narrow_ws(Wq, Xq, batch_index, n_live: int, N: int, K: int, Y,
            "q8_matmul_narrow_ws")
 
 
+def q8_act_buffer_bytes_n(K: int, n_slots: int) -> int:
+    return int(_lib.q8_act_buffer_bytes_n(K, n_slots))
+
+
+def q8_quantize_acts_n(X, n_rows: int, K: int, Xq, n_slots: int, stream=None) -> None:
+    _check(_lib.q8_quantize_acts_n(_ptr(X), n_rows, K, _ptr(Xq), n_slots, _stream(stream)),
+           "q8_quantize_acts_n")
+
+
+def q8_matmul_multi(Wq, Xq, n_slots: int, batch_index, n_live: int, N: int, K: int, Y,
+                    stream=None) -> None:
+    _check(_lib.q8_matmul_multi(_ptr(Wq), _ptr(Xq), n_slots, _ptr(batch_index), n_live, N, K,
+                                _ptr(Y), _stream(stream)), "q8_matmul_multi")
+
+
 def q8_device_supported() -> bool:
     return bool(_lib.q8_device_supported())
 
@@ -189,24 +208,24 @@ def zeroed_workspace(N: int, K: int, device="cuda") -> torch.Tensor | None:
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
-def empty_act_slots(K: int, device="cuda") -> torch.Tensor:
-    nbytes = q8_act_buffer_bytes(K)
+def empty_act_slots(K: int, device="cuda", n_slots: int = Q8_MAX_SLOTS) -> torch.Tensor:
+    nbytes = q8_act_buffer_bytes_n(K, n_slots)
     if nbytes == 0:
-        raise ValueError(f"invalid K={K}")
+        raise ValueError(f"invalid K={K} or n_slots={n_slots}")
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
-def read_act_slots(Xq: torch.Tensor, K: int, stream=None):
+def read_act_slots(Xq: torch.Tensor, K: int, stream=None, n_slots: int = Q8_MAX_SLOTS):
     """All slots of a slot buffer in canonical q8_0 form:
-    (q int8 [16][K], d16 int16 [16][K/32]) device tensors."""
-    q = torch.empty((Q8_MAX_SLOTS, K), dtype=torch.int8, device=Xq.device)
-    d = torch.empty((Q8_MAX_SLOTS, K // Q8_BLOCK), dtype=torch.int16, device=Xq.device)
-    q8_unpack_weights(Xq, Q8_MAX_SLOTS, K, q, d, stream)
+    (q int8 [n_slots][K], d16 int16 [n_slots][K/32]) device tensors."""
+    q = torch.empty((n_slots, K), dtype=torch.int8, device=Xq.device)
+    d = torch.empty((n_slots, K // Q8_BLOCK), dtype=torch.int16, device=Xq.device)
+    q8_unpack_weights(Xq, n_slots, K, q, d, stream)
     return q, d
 
 
 def write_act_slots(Xq: torch.Tensor, K: int, q: torch.Tensor, d16: torch.Tensor,
-                    stream=None) -> None:
-    """Write all 16 slots from canonical q8_0 (q int8 [16][K], d16 int16
-    [16][K/32] binary16 bits)."""
-    q8_pack_weights_q(q, d16, Q8_MAX_SLOTS, K, Xq, stream)
+                    stream=None, n_slots: int = Q8_MAX_SLOTS) -> None:
+    """Write all slots from canonical q8_0 (q int8 [n_slots][K], d16 int16
+    [n_slots][K/32] binary16 bits)."""
+    q8_pack_weights_q(q, d16, n_slots, K, Xq, stream)

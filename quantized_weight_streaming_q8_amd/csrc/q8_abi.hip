@@ -25,6 +25,10 @@ bool valid_shape(int64_t N, int64_t K) {
            N <= kMaxNK / K;
 }
 
+bool valid_slots(int n_slots) {
+    return n_slots >= Q8_MAX_SLOTS && n_slots <= Q8_MAX_COLUMNS && n_slots % Q8_MAX_SLOTS == 0;
+}
+
 bool aligned(const void* p, uintptr_t a) {
     return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }
@@ -64,6 +68,11 @@ size_t q8_act_buffer_bytes(int64_t K) {
     return q8_packed_weight_bytes(Q8_MAX_SLOTS, K);
 }
 
+size_t q8_act_buffer_bytes_n(int64_t K, int n_slots) {
+    if (!valid_slots(n_slots)) return 0;
+    return q8_packed_weight_bytes(n_slots, K);
+}
+
 q8_status q8_pack_weights(const float* W, int64_t N, int64_t K, void* Wq,
                           hipStream_t stream) {
     if (!valid_shape(N, K) || !aligned(W, 16) || !aligned(Wq, 16)) return Q8_ERR_INVALID_ARG;
@@ -90,14 +99,20 @@ q8_status q8_unpack_weights(const void* Wq, int64_t N, int64_t K, int8_t* q,
     return from_hip(q8::launch_unpack_weights(static_cast<const uint8_t*>(Wq), s, q, d16, stream));
 }
 
-q8_status q8_quantize_acts(const float* X, int n_rows, int64_t K, void* Xq,
-                           hipStream_t stream) {
-    if (!valid_shape(1, K) || n_rows < 1 || n_rows > Q8_MAX_SLOTS || !aligned(X, 16) ||
-        !aligned(Xq, 16))
+q8_status q8_quantize_acts_n(const float* X, int n_rows, int64_t K, void* Xq,
+                             int n_slots, hipStream_t stream) {
+    if (!valid_shape(1, K) || !valid_slots(n_slots) || n_rows < 1 || n_rows > n_slots ||
+        !aligned(X, 16) || !aligned(Xq, 16))
         return Q8_ERR_INVALID_ARG;
     if (!current_device_ok()) return Q8_ERR_UNSUPPORTED;
     const q8::Shape s = q8::make_shape(1, K);
-    return from_hip(q8::launch_quantize_acts(X, n_rows, s, static_cast<uint8_t*>(Xq), stream));
+    return from_hip(q8::launch_quantize_acts(X, n_rows, s, static_cast<uint8_t*>(Xq), n_slots,
+                                             stream));
+}
+
+q8_status q8_quantize_acts(const float* X, int n_rows, int64_t K, void* Xq,
+                           hipStream_t stream) {
+    return q8_quantize_acts_n(X, n_rows, K, Xq, Q8_MAX_SLOTS, stream);
 }
 
 q8_status q8_matmul_narrow_path(const void* Wq, const void* Xq,
@@ -114,8 +129,8 @@ q8_status q8_matmul_narrow_path(const void* Wq, const void* Xq,
     const q8::Tiling t = q8::choose_tiling(s);
     const q8::Engine e = path == Q8_PATH_DOT4 ? q8::Engine::kDot4 : q8::Engine::kMfma;
     return from_hip(q8::launch_matmul(e, static_cast<const uint8_t*>(Wq),
-                                      static_cast<const uint8_t*>(Xq), batch_index,
-                                      n_live, s, t, Y, nullptr, stream));
+                                      static_cast<const uint8_t*>(Xq), Q8_MAX_SLOTS,
+                                      batch_index, n_live, s, t, Y, nullptr, stream));
 }
 
 q8_status q8_matmul_narrow(const void* Wq, const void* Xq,
@@ -144,8 +159,23 @@ q8_status q8_matmul_narrow_ws(const void* Wq, const void* Xq,
     if (need > 0 && (!aligned(workspace, 256) || workspace_size < need)) return Q8_ERR_INVALID_ARG;
     if (!current_device_ok()) return Q8_ERR_UNSUPPORTED;
     return from_hip(q8::launch_matmul(q8::Engine::kMfma, static_cast<const uint8_t*>(Wq),
-                                      static_cast<const uint8_t*>(Xq), batch_index, n_live,
-                                      s, t, Y, need > 0 ? workspace : nullptr, stream));
+                                      static_cast<const uint8_t*>(Xq), Q8_MAX_SLOTS,
+                                      batch_index, n_live, s, t, Y,
+                                      need > 0 ? workspace : nullptr, stream));
+}
+
+q8_status q8_matmul_multi(const void* Wq, const void* Xq, int n_slots,
+                          const int32_t* batch_index, int n_live, int64_t N,
+                          int64_t K, float* Y, hipStream_t stream) {
+    if (!valid_shape(N, K) || !valid_slots(n_slots) || n_live < 1 || n_live > n_slots ||
+        !aligned(Wq, 16) || !aligned(Xq, 16) || !aligned(batch_index, 4) || !aligned(Y, 4))
+        return Q8_ERR_INVALID_ARG;
+    if (!current_device_ok()) return Q8_ERR_UNSUPPORTED;
+    const q8::Shape s = q8::make_shape(N, K);
+    const q8::Tiling t = q8::choose_tiling(s);
+    return from_hip(q8::launch_matmul(q8::Engine::kMfma, static_cast<const uint8_t*>(Wq),
+                                      static_cast<const uint8_t*>(Xq), n_slots, batch_index,
+                                      n_live, s, t, Y, nullptr, stream));
 }
 
 int q8_device_supported(void) { return current_device_ok(); }

@@ -34,6 +34,7 @@ namespace q8 {
 
 constexpr int kBlock = 32;        // values per q8_0 block
 constexpr int kMaxSlots = 16;     // activation slots
+constexpr int kMaxColumns = 64;   // slots of a multi-column buffer
 constexpr int kRowsPerGroup = 16; // rows per row group
 constexpr int kScBlocks = 8;      // blocks per super-chunk
 constexpr int kScValues = kScBlocks * kBlock;            // 256
@@ -50,7 +51,7 @@ struct Shape {
     int64_t Kp;   // K padded to a multiple of 256
     int64_t q_bytes;  // packed q region
     int64_t d_bytes;  // packed scale region
-    int64_t act_q_bytes;  // activation buffer: q region (16 rows)
+    int64_t act_q_bytes;  // activation buffer: q region per 16 slots
 };
 
 inline __host__ __device__ int64_t align_up(int64_t v, int64_t a) {
@@ -127,8 +128,9 @@ hipError_t launch_pack_weights_q(const int8_t* q, const uint16_t* d16,
                                  const Shape& s, uint8_t* Wq, hipStream_t st);
 hipError_t launch_unpack_weights(const uint8_t* Wq, const Shape& s, int8_t* q,
                                  uint16_t* d16, hipStream_t st);
+// n_slots (a multiple of 16) is the slot count of the buffer Xq.
 hipError_t launch_quantize_acts(const float* X, int n_rows, const Shape& s,
-                                uint8_t* Xq, hipStream_t st);
+                                uint8_t* Xq, int n_slots, hipStream_t st);
 
 // Matmul tiling: chosen from (N, K) only, so that the fp32 summation order
 // of every output never depends on the live batch.
@@ -146,8 +148,10 @@ size_t workspace_bytes(const Shape& s, const Tiling& t);
 enum class Engine { kMfma, kDot4 };
 // workspace: nullptr for the single-workgroup evaluation of the tree, or a
 // zero-initialised buffer of workspace_bytes() for the split execution.
+// n_slots: slots of the buffer Xq (16; 32, 48 or 64 only with the MFMA
+// engine and no workspace).
 hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
-                         const int32_t* batch_index, int n_live,
+                         int n_slots, const int32_t* batch_index, int n_live,
                          const Shape& s, const Tiling& t, float* Y,
                          void* workspace, hipStream_t st);
 

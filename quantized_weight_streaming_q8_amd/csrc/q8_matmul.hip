@@ -122,6 +122,9 @@ struct MmArgs {
     int KB, NSC, n_live;
     int S, KW;            // summation tree: splits, wave slices per split
     int n_rb;             // row blocks (RG row groups each)
+    int CT;               // slot column tiles (16 slots each)
+    int64_t xq_gs;        // slot buffer: bytes per 16 slots of the q region
+    int64_t xd_gs;        // slot buffer: halves per 16 slots of the scale region
 };
 
 // Super-chunk range [lo, hi) of wave slice k of split s (NSC < 2^16, so 32-bit
@@ -177,54 +180,61 @@ __device__ inline v2i64 ld16_v2_nt(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const v2i64*>(p));
 }
 
-// Operands of one chunk for RG row groups, as loaded.
-template <int RG>
+// Operands of one chunk for RG row groups and CT column tiles of 16 slots.
+template <int RG, int CT>
 struct Chunk {
     v2i64 w[RG];       // weights: this lane's A operands of blocks 2c, 2c+1
     uint4 wd[RG];      // rows 4*tq .. 4*tq+3: binary16 scales of blocks 2c, 2c+1
-    v2i64 aq;          // slot lane & 15: B operands of blocks 2c, 2c+1
-    uint32_t dx;       // slot lane & 15: binary16 scales of blocks 2c, 2c+1
+    v2i64 aq[CT];      // slot 16*ct + (lane & 15): B operands of blocks 2c, 2c+1
+    uint32_t dx[CT];   // the same slot: binary16 scales of blocks 2c, 2c+1
 };
 
 // Chunk cg (global chunk index along K) for RG row groups: weights, their
-// scales, and the slot operands (1 KB contiguous for the wave).
-template <int RG, bool NTW>
-__device__ inline void load_chunk(Chunk<RG>& ch, int cg, const uint8_t* wrow,
+// scales, and the slot operands (1 KB contiguous for the wave per tile).
+template <int RG, int CT, bool NTW>
+__device__ inline void load_chunk(Chunk<RG, CT>& ch, int cg, const uint8_t* wrow,
                                   const uint16_t* wdrow, int64_t g_stride_q,
                                   int64_t g_stride_d, const uint8_t* xa,
-                                  const uint16_t* xdp) {
+                                  const uint16_t* xdp, int64_t xq_gs, int64_t xd_gs) {
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
         const uint8_t* p = wrow + rg * g_stride_q + (int64_t)cg * kChunkBytes;
         ch.w[rg] = NTW ? ld16_v2_nt(p) : ld16_v2(p);
         ch.wd[rg] = ld16(wdrow + rg * g_stride_d + (int64_t)cg * (kChunkDBytes / 2));
     }
-    ch.aq = ld16_v2(xa + (int64_t)cg * kChunkBytes);
-    ch.dx = *reinterpret_cast<const uint32_t*>(xdp + (int64_t)cg * (kChunkDBytes / 2));
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        ch.aq[ct] = ld16_v2(xa + ct * xq_gs + (int64_t)cg * kChunkBytes);
+        ch.dx[ct] = *reinterpret_cast<const uint32_t*>(xdp + ct * xd_gs + (int64_t)cg * (kChunkDBytes / 2));
+    }
 }
 
-// Dot one chunk and accumulate: acc[rg][r] is row 4*tq + r of row group rg
-// for slot lane & 15.  Blocks past K (the padding of the last super-chunk)
-// hold zero codes and zero scales on both sides: their term is
+// Dot one chunk and accumulate: acc[rg][ct][r] is row 4*tq + r of row group
+// rg for slot 16*ct + (lane & 15).  Blocks past K (the padding of the last
+// super-chunk) hold zero codes and zero scales on both sides: their term is
 // fma(0, +0, acc), which returns acc unchanged (acc starts at +0 and no term
 // can make it -0), so they need no test.
-template <int RG>
-__device__ inline void mfma_chunk(const Chunk<RG>& ch, float acc[RG][4]) {
-    const _Float16 dx0 = half_bits(ch.dx, 0), dx1 = half_bits(ch.dx, 1);
+template <int RG, int CT>
+__device__ inline void mfma_chunk(const Chunk<RG, CT>& ch, float acc[RG][CT][4]) {
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-        const v4i zero = {0, 0, 0, 0};
-        const v4i S0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(ch.w[rg].x, ch.aq.x, zero, 0, 0, 0);
-        const v4i S1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(ch.w[rg].y, ch.aq.y, zero, 0, 0, 0);
-        // wd[rg]: row 4*tq + r has its block-2c scale in half 2r, block 2c+1 in 2r+1
-        acc[rg][0] = term_fma(S0[0], half_bits(ch.wd[rg].x, 0), dx0, acc[rg][0]);
-        acc[rg][1] = term_fma(S0[1], half_bits(ch.wd[rg].y, 0), dx0, acc[rg][1]);
-        acc[rg][2] = term_fma(S0[2], half_bits(ch.wd[rg].z, 0), dx0, acc[rg][2]);
-        acc[rg][3] = term_fma(S0[3], half_bits(ch.wd[rg].w, 0), dx0, acc[rg][3]);
-        acc[rg][0] = term_fma(S1[0], half_bits(ch.wd[rg].x, 1), dx1, acc[rg][0]);
-        acc[rg][1] = term_fma(S1[1], half_bits(ch.wd[rg].y, 1), dx1, acc[rg][1]);
-        acc[rg][2] = term_fma(S1[2], half_bits(ch.wd[rg].z, 1), dx1, acc[rg][2]);
-        acc[rg][3] = term_fma(S1[3], half_bits(ch.wd[rg].w, 1), dx1, acc[rg][3]);
+    for (int ct = 0; ct < CT; ++ct) {
+        const _Float16 dx0 = half_bits(ch.dx[ct], 0), dx1 = half_bits(ch.dx[ct], 1);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            const v4i zero = {0, 0, 0, 0};
+            const v4i S0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(ch.w[rg].x, ch.aq[ct].x, zero, 0, 0, 0);
+            const v4i S1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(ch.w[rg].y, ch.aq[ct].y, zero, 0, 0, 0);
+            // wd[rg]: row 4*tq + r has its block-2c scale in half 2r, block 2c+1 in 2r+1
+            float* a = acc[rg][ct];
+            a[0] = term_fma(S0[0], half_bits(ch.wd[rg].x, 0), dx0, a[0]);
+            a[1] = term_fma(S0[1], half_bits(ch.wd[rg].y, 0), dx0, a[1]);
+            a[2] = term_fma(S0[2], half_bits(ch.wd[rg].z, 0), dx0, a[2]);
+            a[3] = term_fma(S0[3], half_bits(ch.wd[rg].w, 0), dx0, a[3]);
+            a[0] = term_fma(S1[0], half_bits(ch.wd[rg].x, 1), dx1, a[0]);
+            a[1] = term_fma(S1[1], half_bits(ch.wd[rg].y, 1), dx1, a[1]);
+            a[2] = term_fma(S1[2], half_bits(ch.wd[rg].z, 1), dx1, a[2]);
+            a[3] = term_fma(S1[3], half_bits(ch.wd[rg].w, 1), dx1, a[3]);
+        }
     }
 }
 
@@ -241,16 +251,17 @@ __device__ inline void coherent_store(float* p, float v) {
 // Output element o of a tile, numbered token-major so that 16 consecutive
 // threads store 16 consecutive rows of one token (64 contiguous bytes):
 // o = (t*RG + rg)*16 + j is token t, row (gbase + rg)*16 + j.  The waves
-// wrote row j = 4*tq + r of slot s at tile element rg*256 + r*64 + tq*16 + s.
+// wrote row j = 4*tq + r of slot s = 16*ct + l at tile element
+// ((rg*CT + ct)*4 + r)*64 + tq*16 + l.
 struct TileOut {
     int t;        // token
     int e;        // tile element of the token's slot column
     int64_t n;    // output row
     bool store;   // inside the matrix, a live token, a row group of this block
-    bool bad;     // the token's slot index is outside [0, 16)
+    bool bad;     // the token's slot index is outside [0, 16*CT)
 };
 
-template <int RG>
+template <int RG, int CT>
 __device__ inline TileOut tile_out(const MmArgs& a, const int* tok_slot, int o,
                                    int64_t gbase, int gskip) {
     TileOut r;
@@ -260,21 +271,23 @@ __device__ inline TileOut tile_out(const MmArgs& a, const int* tok_slot, int o,
     r.n = (gbase + rg) * kRowsPerGroup + j;
     r.store = rg >= gskip && r.t < a.n_live && r.n < a.N;
     const int s = tok_slot[r.t];
-    r.bad = s < 0 || s >= kMaxSlots;
-    r.e = rg * 256 + (j & 3) * 64 + (j >> 2) * 16 + (r.bad ? 0 : s);
+    r.bad = s < 0 || s >= 16 * CT;
+    const int ss = r.bad ? 0 : s;
+    r.e = ((rg * CT + (ss >> 4)) * 4 + (j & 3)) * 64 + (j >> 2) * 16 + (ss & 15);
     return r;
 }
 
 // One workgroup per row block (plain: all S*KW waves) or per (row block,
 // split) (SPLIT: KW waves).  LDS: the wave partials red fp32 [waves][RG*256].
-template <int RG, int D, bool NTW, bool SPLIT>
+template <int RG, int CT, int D, bool NTW, bool SPLIT>
 __global__ void __launch_bounds__(512)
 mm_mfma_kernel(MmArgs a) {
     static_assert(D == 1 || D == 2 || D == 4, "the ring depth must divide a super-chunk");
     static_assert(RG == 1 || RG == 2, "row groups per wave");
     extern __shared__ __align__(16) float red[];
     __shared__ int last_flag;
-    constexpr int E = RG * 256;  // output tile: RG row groups x 16 rows x 16 slots
+    static_assert(CT >= 1 && CT * 16 <= kMaxColumns, "column tiles");
+    constexpr int E = RG * CT * 256;  // output tile: RG row groups x 16 rows x 16*CT slots
     const int lane = threadIdx.x & 63;
     const int tq = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -298,27 +311,29 @@ mm_mfma_kernel(MmArgs a) {
     const uint16_t* xdp = a.xd + (lane & 15) * 2;
     const int gskip = (int)(g0 - gbase);
 
-    float acc[RG][4];
+    float acc[RG][CT][4];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[rg][r] = 0.0f;
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[rg][ct][r] = 0.0f;
 
     // the live tokens' slots, for the output gather: read now, so that the
     // load's latency hides behind the weight stream
-    __shared__ int tok_slot[16];
+    __shared__ int tok_slot[kMaxColumns];
     int my_slot = 0;
-    if (threadIdx.x < 16 && (int)threadIdx.x < a.n_live) my_slot = a.bidx[threadIdx.x];
+    if ((int)threadIdx.x < 16 * CT && (int)threadIdx.x < a.n_live) my_slot = a.bidx[threadIdx.x];
 
-    Chunk<RG> ring[D];
+    Chunk<RG, CT> ring[D];
 #pragma unroll
-    for (int i = 0; i < D; ++i) load_chunk<RG, NTW>(ring[i], c_lo + i, wrow, wdrow, gq, gd, xa, xdp);
+    for (int i = 0; i < D; ++i) load_chunk<RG, CT, NTW>(ring[i], c_lo + i, wrow, wdrow, gq, gd, xa, xdp, a.xq_gs, a.xd_gs);
     int c = c_lo;
     for (; c + D < c_hi; c += D) {
 #pragma unroll
         for (int i = 0; i < D; ++i) {
-            mfma_chunk<RG>(ring[i], acc);
-            load_chunk<RG, NTW>(ring[i], c + D + i, wrow, wdrow, gq, gd, xa, xdp);
+            mfma_chunk<RG, CT>(ring[i], acc);
+            load_chunk<RG, CT, NTW>(ring[i], c + D + i, wrow, wdrow, gq, gd, xa, xdp, a.xq_gs, a.xd_gs);
             // keep each chunk's loads right after its dot: left alone, the
             // scheduler sinks all D chunks' loads to the end of the turn,
             // and every turn then waits a full memory latency
@@ -326,19 +341,22 @@ mm_mfma_kernel(MmArgs a) {
         }
     }
 #pragma unroll
-    for (int i = 0; i < D; ++i) mfma_chunk<RG>(ring[i], acc);
+    for (int i = 0; i < D; ++i) mfma_chunk<RG, CT>(ring[i], acc);
 
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[(w * RG + rg) * 256 + r * 64 + lane] = acc[rg][r];
-    if (threadIdx.x < 16) tok_slot[threadIdx.x] = my_slot;
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                red[((w * RG + rg) * CT + ct) * 256 + r * 64 + lane] = acc[rg][ct][r];
+    if ((int)threadIdx.x < 16 * CT) tok_slot[threadIdx.x] = my_slot;
     __syncthreads();
 
     const int nthreads = nwaves * 64;
     if (!SPLIT) {
         for (int o = threadIdx.x; o < E; o += nthreads) {
-            const TileOut to = tile_out<RG>(a, tok_slot, o, gbase, gskip);
+            const TileOut to = tile_out<RG, CT>(a, tok_slot, o, gbase, gskip);
             if (to.store)
                 a.Y[(int64_t)to.t * a.N + to.n] =
                     to.bad ? __builtin_nanf("") : tree_sum(red, E, to.e, a.S, a.KW);
@@ -364,7 +382,7 @@ mm_mfma_kernel(MmArgs a) {
     if (!last_flag) return;
     // the last split to arrive: level 2 in split order, then rearm the counter
     for (int o = threadIdx.x; o < E; o += nthreads) {
-        const TileOut to = tile_out<RG>(a, tok_slot, o, gbase, gskip);
+        const TileOut to = tile_out<RG, CT>(a, tok_slot, o, gbase, gskip);
         if (!to.store) continue;
         float y = coherent_load(a.part + (int64_t)rb * E + to.e);
         for (int s = 1; s < a.S; ++s) y += coherent_load(a.part + ((int64_t)s * a.n_rb + rb) * E + to.e);
@@ -375,19 +393,20 @@ mm_mfma_kernel(MmArgs a) {
 
 int mfma_waves(const MmArgs& a, bool split) { return split ? a.KW : a.S * a.KW; }
 
-size_t mfma_lds_bytes(const MmArgs& a, int rg, bool split) {
-    return (size_t)mfma_waves(a, split) * rg * 256 * sizeof(float);
+size_t mfma_lds_bytes(const MmArgs& a, int rg, int ct, bool split) {
+    return (size_t)mfma_waves(a, split) * rg * ct * 256 * sizeof(float);
 }
 
 int mfma_max_waves(int) { return 8; }  // 512 threads: 256 VGPRs per lane
 
-template <int RG, int D, bool NTW, bool SPLIT>
+template <int RG, int CT, int D, bool NTW, bool SPLIT>
 hipError_t launch_mfma(const MmArgs& a, hipStream_t st) {
     const int waves = mfma_waves(a, SPLIT);
-    const size_t lds = mfma_lds_bytes(a, RG, SPLIT);
-    if (lds > kMaxLds || waves > mfma_max_waves(RG) || a.G < RG) return hipErrorInvalidValue;
+    const size_t lds = mfma_lds_bytes(a, RG, CT, SPLIT);
+    if (lds > kMaxLds || waves > mfma_max_waves(RG) || a.G < RG || a.CT != CT)
+        return hipErrorInvalidValue;
     const unsigned grid = (unsigned)(SPLIT ? (int64_t)a.n_rb * a.S : a.n_rb);
-    hipLaunchKernelGGL((mm_mfma_kernel<RG, D, NTW, SPLIT>), dim3(grid), dim3(64 * waves), lds, st, a);
+    hipLaunchKernelGGL((mm_mfma_kernel<RG, CT, D, NTW, SPLIT>), dim3(grid), dim3(64 * waves), lds, st, a);
     return hipGetLastError();
 }
 
@@ -554,14 +573,18 @@ size_t workspace_bytes(const Shape& s, const Tiling& t) {
 }
 
 hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
-                         const int32_t* batch_index, int n_live,
+                         int n_slots, const int32_t* batch_index, int n_live,
                          const Shape& s, const Tiling& t, float* Y,
                          void* workspace, hipStream_t st) {
     MmArgs a;
+    a.CT = n_slots / kMaxSlots;
+    if (a.CT < 1 || a.CT * kMaxSlots != n_slots || n_slots > kMaxColumns) return hipErrorInvalidValue;
     a.wq = Wq;
     a.wd = reinterpret_cast<const uint16_t*>(Wq + s.q_bytes);
     a.xq = Xq;
-    a.xd = reinterpret_cast<const uint16_t*>(Xq + s.act_q_bytes);
+    a.xd = reinterpret_cast<const uint16_t*>(Xq + a.CT * s.act_q_bytes);
+    a.xq_gs = s.act_q_bytes;
+    a.xd_gs = s.NSC * 4 * (kChunkDBytes / 2);
     a.bidx = batch_index;
     a.Y = Y;
     a.N = s.N;
@@ -572,8 +595,9 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
     a.S = t.splits;
     a.KW = t.kw;
     if (a.S * a.KW > a.NSC) return hipErrorInvalidValue;
-    if (e == Engine::kDot4) return launch_dot4(a, st);
+    if (e == Engine::kDot4) return a.CT == 1 ? launch_dot4(a, st) : hipErrorInvalidValue;
     const bool split = workspace != nullptr && t.splits > 1;
+    if (split && a.CT != 1) return hipErrorInvalidValue;
     const int rg = launch_rg(s, t, split);
     a.n_rb = (int)((s.G + rg - 1) / rg);
     a.counters = nullptr;
@@ -583,16 +607,50 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
         a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
                                           align_up((int64_t)a.n_rb * 4, 256));
     }
-#define Q8_LAUNCH(R, N, P) return launch_mfma<R, kRing, N, P>(a, st)
-    if (rg == 2) {
-        if (split) { if (t.nt_weights) Q8_LAUNCH(2, true, true); Q8_LAUNCH(2, false, true); }
-        if (t.nt_weights) Q8_LAUNCH(2, true, false);
-        Q8_LAUNCH(2, false, false);
+    // more than one column tile: a shallower ring keeps the chunk operands
+    // (which grow with the tiles) in registers
+    if (a.CT > 1) {
+#ifdef Q8_TUNING
+        // measurement builds only: rows and ring depth of the wide tiles
+        const int mrg = getenv("Q8_MT_RG") ? atoi(getenv("Q8_MT_RG")) : rg;
+        const int md = getenv("Q8_MT_D") ? atoi(getenv("Q8_MT_D")) : 2;
+        if (mrg == 1 || mrg == 2) {
+            a.n_rb = (int)((s.G + mrg - 1) / mrg);
+#define Q8_T(C, R, D) if (a.CT == C && mrg == R && md == D) return launch_mfma<R, C, D, true, false>(a, st);
+            Q8_T(2, 1, 1) Q8_T(2, 1, 2) Q8_T(2, 1, 4) Q8_T(2, 2, 1) Q8_T(2, 2, 2) Q8_T(2, 2, 4)
+            Q8_T(4, 1, 1) Q8_T(4, 1, 2) Q8_T(4, 1, 4) Q8_T(4, 2, 1) Q8_T(4, 2, 2) Q8_T(4, 2, 4)
+#undef Q8_T
+        }
+#endif
+        // measured on MI355X: many row blocks (large N) run best with one
+        // row group and two chunks in flight per wave (more waves), few with
+        // two row groups and four chunks
+        const bool wide = (s.G + 1) / 2 >= 512 || rg == 1;
+        a.n_rb = (int)(wide ? s.G : (s.G + 1) / 2);
+#define Q8_LAUNCH_CT(C, D2)                                                     \
+    case C:                                                                     \
+        return wide ? launch_mfma<1, C, 2, true, false>(a, st)                  \
+                    : launch_mfma<2, C, D2, true, false>(a, st);
+        switch (a.CT) {
+            Q8_LAUNCH_CT(2, 4)
+            Q8_LAUNCH_CT(3, 2)  // three tiles and four chunks do not fit the registers
+            Q8_LAUNCH_CT(4, 4)
+            default: return hipErrorInvalidValue;
+        }
+#undef Q8_LAUNCH_CT
     }
-    if (split) { if (t.nt_weights) Q8_LAUNCH(1, true, true); Q8_LAUNCH(1, false, true); }
-    if (t.nt_weights) Q8_LAUNCH(1, true, false);
-    Q8_LAUNCH(1, false, false);
-#undef Q8_LAUNCH
+#ifdef Q8_TUNING
+    if (!t.nt_weights) {
+        if (rg == 2) return split ? launch_mfma<2, 1, kRing, false, true>(a, st)
+                                  : launch_mfma<2, 1, kRing, false, false>(a, st);
+        return split ? launch_mfma<1, 1, kRing, false, true>(a, st)
+                     : launch_mfma<1, 1, kRing, false, false>(a, st);
+    }
+#endif
+    if (rg == 2) return split ? launch_mfma<2, 1, kRing, true, true>(a, st)
+                              : launch_mfma<2, 1, kRing, true, false>(a, st);
+    return split ? launch_mfma<1, 1, kRing, true, true>(a, st)
+                 : launch_mfma<1, 1, kRing, true, false>(a, st);
 }
 
 }  // namespace q8

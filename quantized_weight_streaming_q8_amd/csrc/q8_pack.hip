@@ -6,7 +6,8 @@
 // -- the narrow-batch matmul" (32-weight blocks, pre-quantised activations),
 // read as the GGUF q8_0 block: d = absmax/127 in binary32, q = round half away
 // from zero of x/d (IEEE division), clamped to +-127, d stored as binary16.
-// The activation slot buffer uses the packed layout of a 16-row matrix.
+// An activation slot buffer of n_slots slots uses the packed layout of an
+// n_slots-row matrix (row = slot).
 //
 // Thread mapping, all kernels: one lane per 8-value segment, 4 consecutive
 // lanes per 32-value block, consecutive blocks of a row on consecutive lane
@@ -109,7 +110,7 @@ unpack_weights_kernel(const uint8_t* __restrict__ wq, const uint16_t* __restrict
     if (ix.seg == 0) d16[ix.row * KB + ix.blk] = wd[packed_d_index(ix.row, ix.blk, NSC)];
 }
 
-// Activations go to the packed layout of a 16-row matrix (row = slot); only
+// Activations go to the packed layout of an n_slots-row matrix (row = slot); only
 // rows < n_rows are written.
 __global__ void __launch_bounds__(kThreads)
 quantize_acts_kernel(const float* __restrict__ X, int64_t K, int64_t KB,
@@ -160,9 +161,9 @@ hipError_t launch_unpack_weights(const uint8_t* Wq, const Shape& s, int8_t* q,
 }
 
 hipError_t launch_quantize_acts(const float* X, int n_rows, const Shape& s,
-                                uint8_t* Xq, hipStream_t st) {
+                                uint8_t* Xq, int n_slots, hipStream_t st) {
     const int64_t total = (int64_t)n_rows * s.NSC * kScBlocks * 4;
-    uint16_t* xd = reinterpret_cast<uint16_t*>(Xq + s.act_q_bytes);
+    uint16_t* xd = reinterpret_cast<uint16_t*>(Xq + (n_slots / kMaxSlots) * s.act_q_bytes);
     hipLaunchKernelGGL(quantize_acts_kernel, dim3(grid_for(total)), dim3(kThreads),
                        0, st, X, s.K, s.KB, s.NSC, total, Xq, xd);
     return hipGetLastError();

@@ -29,7 +29,7 @@ def test_header_declares_the_abi():
     names = header_functions()
     for core in ("q8_pack_weights", "q8_quantize_acts", "q8_matmul_narrow"):
         assert core in names
-    assert len(names) == 12, names
+    assert len(names) == 15, names
 
 
 def test_every_declared_symbol_is_exported(q8):
@@ -43,6 +43,7 @@ def test_constants_agree_with_header(q8):
     text = open(HEADER).read()
     assert int(re.search(r"#define Q8_MAX_SLOTS (\d+)", text).group(1)) == q8.Q8_MAX_SLOTS == 16
     assert int(re.search(r"#define Q8_BLOCK (\d+)", text).group(1)) == q8.Q8_BLOCK == 32
+    assert int(re.search(r"#define Q8_MAX_COLUMNS (\d+)", text).group(1)) == q8.Q8_MAX_COLUMNS == 64
     for name in ("Q8_OK", "Q8_ERR_INVALID_ARG", "Q8_ERR_UNSUPPORTED", "Q8_ERR_HIP",
                  "Q8_PATH_AUTO", "Q8_PATH_MFMA", "Q8_PATH_DOT4"):
         val = int(re.search(name + r"\s*=\s*(\d+)", text).group(1))
@@ -166,3 +167,33 @@ def test_binding_raises_on_rejected_call(q8):
         q8.q8_matmul_narrow(P, P, P, 0, 64, 64, P, stream=0)
     assert e.value.status == q8.Q8_ERR_INVALID_ARG
     assert "Q8_ERR_INVALID_ARG" in str(e.value)
+
+
+@pytest.mark.parametrize("K", [32, 768, 5120, 17408])
+def test_multi_column_buffer_sizes(q8, K):
+    for n in (16, 32, 48, 64):
+        assert q8.q8_act_buffer_bytes_n(K, n) == q8.q8_packed_weight_bytes(n, K)
+        assert q8.q8_act_buffer_bytes_n(K, n) == (n // 16) * q8.q8_act_buffer_bytes(K)
+    for bad in (0, 8, 17, 24, 80, -16):
+        assert q8.q8_act_buffer_bytes_n(K, bad) == 0
+
+
+def test_multi_column_calls_reject_invalid_arguments(q8):
+    lib = q8.library()
+    bad = q8.Q8_ERR_INVALID_ARG
+    # slot counts that are not 16, 32, 48 or 64
+    for n_slots in (0, 8, 24, 80):
+        assert lib.q8_quantize_acts_n(P, 4, 64, P, n_slots, None) == bad
+        assert lib.q8_matmul_multi(P, P, n_slots, P, 4, 64, 64, P, None) == bad
+    # more rows or live tokens than slots
+    assert lib.q8_quantize_acts_n(P, 33, 64, P, 32, None) == bad
+    assert lib.q8_quantize_acts_n(P, 0, 64, P, 32, None) == bad
+    assert lib.q8_matmul_multi(P, P, 32, P, 33, 64, 64, P, None) == bad
+    assert lib.q8_matmul_multi(P, P, 64, P, 0, 64, 64, P, None) == bad
+    # shapes, null and misaligned pointers
+    assert lib.q8_matmul_multi(P, P, 64, P, 4, 64, 48, P, None) == bad
+    assert lib.q8_matmul_multi(None, P, 64, P, 4, 64, 64, P, None) == bad
+    assert lib.q8_matmul_multi(P, P + 8, 64, P, 4, 64, 64, P, None) == bad
+    assert lib.q8_matmul_multi(P, P, 64, P + 2, 4, 64, 64, P, None) == bad
+    assert lib.q8_matmul_multi(P, P, 64, P, 4, 64, 64, P + 1, None) == bad
+    assert lib.q8_quantize_acts_n(P + 4, 4, 64, P, 64, None) == bad
