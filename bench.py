@@ -73,7 +73,7 @@ def step_bytes(matrices, n_live: int) -> int:
 class Layer:
     """R packed copies of a workload's matrices, plus the activation buffers."""
 
-    def __init__(self, key: str):
+    def __init__(self, key: str, fused: bool = False):
         import torch
         import quantized_weight_streaming_q8_amd as q8
         self.q8 = q8
@@ -82,7 +82,8 @@ class Layer:
         one = sum(q8.q8_packed_weight_bytes(m.N, m.K) for m in self.mats)
         self.copies = max(1, -(-COLD_BYTES // one))
         self.packed = [[None] * len(self.mats) for _ in range(self.copies)]
-        self.X, self.Xq, self.Y, self.ws = [], [], [], []
+        self.fused = fused
+        self.X, self.Xq, self.Y, self.ws, self.fws = [], [], [], [], []
         for i, m in enumerate(self.mats):
             W = torch.from_numpy(wl.weights(self.w.config, i, m.N, m.K)).cuda()
             base = q8.empty_packed_weights(m.N, m.K)
@@ -95,6 +96,7 @@ class Layer:
             self.Xq.append(q8.empty_act_slots(m.K))
             self.Y.append(torch.empty((16, m.N), dtype=torch.float32, device="cuda"))
             self.ws.append(q8.zeroed_workspace(m.N, m.K))
+            self.fws.append(q8.zeroed_fused_workspace(m.N, m.K))
         torch.cuda.synchronize()
         self.packed_bytes = one
 
@@ -104,15 +106,21 @@ class Layer:
         return torch.from_numpy(bi).cuda()
 
     def step(self, copy: int, bi, n_live: int, events=None) -> None:
-        """Enqueue one step; with `events`, bracket every matmul launch with
-        a pair of events recorded on the launch stream."""
+        """Enqueue one step: for every matrix, pre-quantise the 16 slots and
+        run the narrow matmul, either in one fused launch or as the two
+        separate calls; with `events`, bracket every matrix's launches with a
+        pair of events recorded on the launch stream."""
         q8 = self.q8
         for i, m in enumerate(self.mats):
-            q8.q8_quantize_acts(self.X[i], 16, m.K, self.Xq[i])
             if events is not None:
                 events[i][0].record()
-            q8.q8_matmul_narrow_ws(self.packed[copy][i], self.Xq[i], bi, n_live, m.N, m.K,
-                                   self.Y[i], self.ws[i])
+            if self.fused:
+                q8.q8_matmul_narrow_fused(self.packed[copy][i], self.X[i], 16, self.Xq[i], bi,
+                                          n_live, m.N, m.K, self.Y[i], self.fws[i])
+            else:
+                q8.q8_quantize_acts(self.X[i], 16, m.K, self.Xq[i])
+                q8.q8_matmul_narrow_ws(self.packed[copy][i], self.Xq[i], bi, n_live, m.N, m.K,
+                                       self.Y[i], self.ws[i])
             if events is not None:
                 events[i][1].record()
 
@@ -229,6 +237,15 @@ def kernel_avg_us(layer: Layer, i: int, n_live: int, launches: int) -> float:
         layer.Y[i], layer.ws[i]), launches)
 
 
+def fused_avg_us(layer: Layer, i: int, n_live: int, launches: int) -> float:
+    """Average duration of one fused pre-quantise + matmul launch of matrix i."""
+    q8, m = layer.q8, layer.mats[i]
+    bi = layer.batch_index(n_live)
+    return graph_avg_us(lambda c: q8.q8_matmul_narrow_fused(
+        layer.packed[c % layer.copies][i], layer.X[i], 16, layer.Xq[i], bi, n_live, m.N, m.K,
+        layer.Y[i], layer.fws[i]), launches)
+
+
 def quantize_avg_us(layer: Layer, i: int, launches: int = 100) -> float:
     """Average duration of one pre-quantize launch (16 rows of matrix i's K)."""
     q8, m = layer.q8, layer.mats[i]
@@ -303,10 +320,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(n_live: int):
+def pmc_summary_path(fused: bool) -> str:
+    name = "gate_up_fused_qwen3_layer_pmc.json" if fused else "gate_up_matmul_qwen3_layer_pmc.json"
+    return os.path.join(PROFILE_DIR, name)
+
+
+def measured_traffic(n_live: int, fused: bool):
     """HBM bytes per launch of the dominant kernel from the committed PMC
     counter summary, if it was taken on the current kernel source."""
-    path = os.path.join(PROFILE_DIR, "gate_up_matmul_qwen3_layer_pmc.json")
+    path = pmc_summary_path(fused)
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -389,8 +411,9 @@ def engine_ab(layer: Layer, n_values, launches: int) -> dict:
 CAL_BYTES = 256 << 20
 
 
-def pmc_probe(launches: int, n_live: int) -> None:
-    """The dominant matmul of the Layer workload, `launches` times over two
+def pmc_probe(launches: int, n_live: int, fused: bool) -> None:
+    """The dominant kernel of the Layer workload's step (the fused
+    pre-quantise + matmul, or the matmul alone), `launches` times over two
     weight copies, then the calibration copy three times."""
     import torch
     import quantized_weight_streaming_q8_amd as q8
@@ -407,9 +430,13 @@ def pmc_probe(launches: int, n_live: int) -> None:
     q8.q8_quantize_acts(X, 16, m.K, Xq)
     Y = torch.empty((16, m.N), dtype=torch.float32, device="cuda")
     ws = q8.zeroed_workspace(m.N, m.K)
+    fws = q8.zeroed_fused_workspace(m.N, m.K)
     bi = torch.from_numpy(wl.batch_index(w.config, n_live, random=w.random_batch_index)).cuda()
     for c in range(launches):
-        q8.q8_matmul_narrow_ws(packed[c % 2], Xq, bi, n_live, m.N, m.K, Y, ws)
+        if fused:
+            q8.q8_matmul_narrow_fused(packed[c % 2], X, 16, Xq, bi, n_live, m.N, m.K, Y, fws)
+        else:
+            q8.q8_matmul_narrow_ws(packed[c % 2], Xq, bi, n_live, m.N, m.K, Y, ws)
     torch.cuda.synchronize()
     a = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
@@ -417,8 +444,8 @@ def pmc_probe(launches: int, n_live: int) -> None:
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(f"pmc probe: {launches} launches of {m.name} at n_live={n_live}, 3 copies of {CAL_BYTES} B",
-          flush=True)
+    print(f"pmc probe: {launches} {'fused' if fused else 'matmul'} launches of {m.name} at "
+          f"n_live={n_live}, 3 copies of {CAL_BYTES} B", flush=True)
 
 
 def _counter_rows(path: str, counter: str):
@@ -427,10 +454,10 @@ def _counter_rows(path: str, counter: str):
         return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
 
 
-def pmc_summarize(fetch_csv: str, write_csv: str, n_live: int, out: str) -> dict:
-    """Per-launch HBM bytes of the dominant matmul from the two counter
+def pmc_summarize(fetch_csv: str, write_csv: str, n_live: int, fused: bool, out: str) -> dict:
+    """Per-launch HBM bytes of the dominant kernel from the two counter
     passes, each scaled by the calibration copy."""
-    res = {"kernel_source_hash": kernel_source_hash(), "n_live": n_live,
+    res = {"kernel_source_hash": kernel_source_hash(), "n_live": n_live, "fused": fused,
            "calibration_copy_bytes": CAL_BYTES}
     per = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -476,6 +503,9 @@ def main(argv=None) -> int:
                          "calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two counter_collection.csv files")
+    ap.add_argument("--fused", action="store_true",
+                    help="run the step through the fused pre-quantise + matmul entry point "
+                         "(one launch per matrix; default: separate launches, faster here)")
     ap.add_argument("--no-multi", dest="multi", action="store_false",
                     help="skip the 16..64-column multi-token measurement")
     ap.add_argument("--engine-ab", action="store_true",
@@ -483,8 +513,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.pmc_summarize:
-        path = os.path.join(PROFILE_DIR, "gate_up_matmul_qwen3_layer_pmc.json")
-        print(json.dumps(pmc_summarize(*args.pmc_summarize, args.n_live, path), indent=1))
+        path = pmc_summary_path(args.fused)
+        print(json.dumps(pmc_summarize(*args.pmc_summarize, args.n_live, args.fused, path), indent=1))
         return 0
 
     if args.gpus != 1:
@@ -498,9 +528,9 @@ def main(argv=None) -> int:
     import torch
     torch.cuda.set_device(0)
     if args.pmc_probe:
-        pmc_probe(args.pmc_probe, args.n_live)
+        pmc_probe(args.pmc_probe, args.n_live, args.fused)
         return 0
-    layer = Layer(args.workload)
+    layer = Layer(args.workload, fused=args.fused)
     mats = layer.mats
     if args.engine_ab:
         res = engine_ab(layer, (1, 2, 4, 8, 16), max(16, 2 * layer.copies))
@@ -513,57 +543,76 @@ def main(argv=None) -> int:
     print(f"# {args.workload}: {len(mats)} matrices, {layer.packed_bytes / 1e6:.1f} MB packed, "
           f"{layer.copies} copies rotated", file=sys.stderr, flush=True)
 
-    ms_eager, _ = time_steps(layer, args.n_live, args.steps, args.warmup, with_events=False)
-    graph_ok = None
-    ms = ms_eager
-    if args.graph:
-        ms_graph, graph_ok = time_graph_steps(layer, args.n_live, args.steps, args.warmup)
-        if graph_ok and ms_graph < ms_eager:
-            ms = ms_graph
+    def step_time(n_live, steps, warmup):
+        """(ms per step, eager ms, graph ms or None): the faster of eager
+        launches and graph replay (the replay checked against eager)."""
+        ms_e, _ = time_steps(layer, n_live, steps, warmup, with_events=False)
+        ms_g = None
+        if args.graph:
+            ms_g, ok = time_graph_steps(layer, n_live, steps, warmup)
+            if not ok:
+                ms_g = None
+        best = ms_e if ms_g is None or ms_e <= ms_g else ms_g
+        return best, ms_e, ms_g
+
+    # the step the library's fused entry point runs (one launch per matrix),
+    # and the same step as separate pre-quantise and matmul launches
+    layer.fused = args.fused
+    ms, ms_eager, ms_graph = step_time(args.n_live, args.steps, args.warmup)
+    layer.fused = not args.fused
+    ms_other, _, _ = step_time(args.n_live, args.steps, args.warmup)
+    layer.fused = args.fused
     nbytes = step_bytes(mats, args.n_live)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    print(f"# n_live={args.n_live}: {ms * 1e3:.1f} us/step ({'graph' if ms is not ms_eager else 'eager'}), "
-          f"eager {ms_eager * 1e3:.1f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    print(f"# n_live={args.n_live}: {ms * 1e3:.1f} us/step "
+          f"({'fused' if args.fused else 'separate'} launches; eager {ms_eager * 1e3:.1f}"
+          f"{'' if ms_graph is None else f', graph {ms_graph * 1e3:.1f}'}), {gbs:.0f} GB/s; "
+          f"{'separate' if args.fused else 'fused'}: {ms_other * 1e3:.1f} us/step",
+          file=sys.stderr, flush=True)
 
     # each kernel alone: back-to-back launches between one pair of events
     launches = max(64, 4 * layer.copies)
     per_matrix = {}
-    kern_us = []
+    kern_us, fused_us = [], []
     for i, m in enumerate(mats):
         us = kernel_avg_us(layer, i, args.n_live, launches)
+        fu = fused_avg_us(layer, i, args.n_live, launches)
         kern_us.append(us)
+        fused_us.append(fu)
         b = matmul_bytes(m.N, m.K, args.n_live)
+        fb = b + quantize_bytes(m.K)
         per_matrix[m.name] = {
             "K": m.K, "N": m.N, "us": round(us, 2), "GBps": round(b / us / 1e3, 1),
             "frac_peak": round(b / us / 1e3 / PEAK_HBM_GBS, 4),
             "quantize_us": round(quantize_avg_us(layer, i), 2),
+            "fused_us": round(fu, 2), "fused_GBps": round(fb / fu / 1e3, 1),
         }
     mm_bytes = sum(matmul_bytes(m.N, m.K, args.n_live) for m in mats)
     print(f"# matmuls alone: {sum(kern_us):.1f} us, {mm_bytes / sum(kern_us) / 1e3:.0f} GB/s; "
           + ", ".join(f"{m.name} {u:.2f} us" for m, u in zip(mats, kern_us)), file=sys.stderr, flush=True)
+    print("# fused pre-quantise + matmul: "
+          + ", ".join(f"{m.name} {u:.2f} us" for m, u in zip(mats, fused_us)), file=sys.stderr, flush=True)
 
+    # roofline of the dominant kernel of the step as run
     dom = [i for i, m in enumerate(mats) if m.name == DOMINANT]
     di = dom[0] if dom else int(np.argmax([m.N * m.K for m in mats]))
     dm = mats[di]
-    dom_bytes = matmul_bytes(dm.N, dm.K, args.n_live)
-    dom_us = kern_us[di]
+    dom_bytes = matmul_bytes(dm.N, dm.K, args.n_live) + (quantize_bytes(dm.K) if args.fused else 0)
+    dom_us = fused_us[di] if args.fused else kern_us[di]
     achieved = dom_bytes / dom_us / 1e3
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-        "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(args.n_live),
-        "kernel": f"q8 narrow matmul, {dm.name} {dm.K}->{dm.N}, n_live={args.n_live}",
+        "frac": round(achieved / PEAK_HBM_GBS, 4),
+        "traffic": measured_traffic(args.n_live, args.fused),
+        "kernel": (f"fused pre-quantise + q8 narrow matmul" if args.fused else "q8 narrow matmul")
+        + f", {dm.name} {dm.K}->{dm.N}, n_live={args.n_live}",
         "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 2),
     }
 
     sweep = {}
     if args.sweep_steps > 0:
         for n in range(1, 17):
-            ms_e, _ = time_steps(layer, n, args.sweep_steps, min(args.warmup, 20), with_events=False)
-            ms_n = ms_e
-            if args.graph:
-                ms_g, ok = time_graph_steps(layer, n, args.sweep_steps, min(args.warmup, 20))
-                if ok and ms_g < ms_e:
-                    ms_n = ms_g
+            ms_n, ms_e, _ = step_time(n, args.sweep_steps, min(args.warmup, 20))
             kn = [kernel_avg_us(layer, i, n, max(16, 2 * layer.copies)) for i in range(len(mats))]
             sweep[n] = {"ms_per_step": round(ms_n, 4), "ms_per_step_eager": round(ms_e, 4),
                         "GBps": round(step_bytes(mats, n) / (ms_n * 1e-3) / 1e9, 1),
@@ -597,7 +646,10 @@ def main(argv=None) -> int:
         "ms_per_step_eager": round(ms_eager, 5),
         "timing": ("hip graph replay per step (checked bit-identical to eager)" if ms is not ms_eager
                    else "eager launches on one stream") + "; the faster of the two",
-        "ms_per_step_graph": round(ms_graph, 5) if args.graph else None,
+        "ms_per_step_graph": round(ms_graph, 5) if ms_graph is not None else None,
+        "step_launches": "fused pre-quantise + matmul, one launch per matrix" if args.fused
+        else "separate pre-quantise and matmul launches",
+        "ms_per_step_other": round(ms_other, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

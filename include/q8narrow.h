@@ -167,6 +167,35 @@ q8_status q8_matmul_narrow_ws(const void* Wq, const void* Xq,
                               int64_t N, int64_t K, float* Y, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------- fused pre-quantisation */
+
+/* Bytes of workspace q8_matmul_narrow_fused needs for an N x K matrix (64 KB
+ * of counters and flags, then q8_matmul_workspace_bytes(N, K)); 0 if the
+ * shape is invalid. */
+size_t q8_matmul_fused_workspace_bytes(int64_t N, int64_t K);
+
+/* q8_quantize_acts(X, n_rows, K, Xq) followed by q8_matmul_narrow_ws(Wq, Xq,
+ * batch_index, n_live, N, K, Y, workspace) in one launch, with the same
+ * results: Xq receives the same bits as q8_quantize_acts would write and Y
+ * the same bits as the matmul.  "Batched decode: co-decode N live sessions
+ * in one GPU pass" (antirez/ds4 PR #530), commit "CUDA: add pos-vector RoPE
+ * tail variants", measures a couple of microseconds per extra launch, which
+ * adds up over a decode step; this removes the pre-quantiser's launch (the
+ * activations are small next to the weights: section "Why it's worth it --
+ * the narrow-batch matmul").  A few workgroups of the launch quantise X and
+ * publish the slots; the matmul workgroups stream their first weights while
+ * they wait for them.
+ *
+ * workspace: device memory, 256-byte aligned, at least
+ * q8_matmul_fused_workspace_bytes(N, K) bytes, zero-filled before its first
+ * use; every completed call leaves it zero again.  It must not be shared by
+ * calls that can run at the same time.  1 <= n_rows, n_live <= Q8_MAX_SLOTS;
+ * X fp32 [n_rows][K], 16-byte aligned. */
+q8_status q8_matmul_narrow_fused(const void* Wq, const float* X, int n_rows, void* Xq,
+                                 const int32_t* batch_index, int n_live, int64_t N,
+                                 int64_t K, float* Y, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------- multi-token columns */
 
 /* Several tokens per sequence in one step: "[feature] Enable Dynamic

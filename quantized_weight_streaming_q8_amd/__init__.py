@@ -45,6 +45,9 @@ _SIGNATURES = {
     "q8_matmul_narrow_path": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp, _i32], _i32),
     "q8_matmul_workspace_bytes": ([_i64, _i64], ctypes.c_size_t),
     "q8_matmul_narrow_ws": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp], _i32),
+    "q8_matmul_fused_workspace_bytes": ([_i64, _i64], ctypes.c_size_t),
+    "q8_matmul_narrow_fused": ([_vp, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _vp, _vp,
+                                ctypes.c_size_t, _vp], _i32),
     "q8_act_buffer_bytes_n": ([_i64, _i32], ctypes.c_size_t),
     "q8_quantize_acts_n": ([_vp, _i32, _i64, _vp, _i32, _vp], _i32),
     "q8_matmul_multi": ([_vp, _vp, _i32, _vp, _i32, _i64, _i64, _vp, _vp], _i32),
@@ -171,6 +174,20 @@ def q8_matmul_narrow_ws(Wq, Xq, batch_index, n_live: int, N: int, K: int, Y,
            "q8_matmul_narrow_ws")
 
 
+def q8_matmul_fused_workspace_bytes(N: int, K: int) -> int:
+    return int(_lib.q8_matmul_fused_workspace_bytes(N, K))
+
+
+def q8_matmul_narrow_fused(Wq, X, n_rows: int, Xq, batch_index, n_live: int, N: int, K: int,
+                           Y, workspace, workspace_bytes: int | None = None,
+                           stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.q8_matmul_narrow_fused(_ptr(Wq), _ptr(X), n_rows, _ptr(Xq), _ptr(batch_index),
+                                       n_live, N, K, _ptr(Y), _ptr(workspace), workspace_bytes,
+                                       _stream(stream)), "q8_matmul_narrow_fused")
+
+
 def q8_act_buffer_bytes_n(K: int, n_slots: int) -> int:
     return int(_lib.q8_act_buffer_bytes_n(K, n_slots))
 
@@ -205,6 +222,14 @@ def zeroed_workspace(N: int, K: int, device="cuda") -> torch.Tensor | None:
     nbytes = q8_matmul_workspace_bytes(N, K)
     if nbytes == 0:
         return None
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def zeroed_fused_workspace(N: int, K: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for q8_matmul_narrow_fused."""
+    nbytes = q8_matmul_fused_workspace_bytes(N, K)
+    if nbytes == 0:
+        raise ValueError(f"invalid shape N={N} K={K}")
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 

@@ -81,6 +81,28 @@ __host__ __device__ constexpr int pos_slot(int pos8) {
     return ((pos8 & 1) << 1) | (pos8 >> 1);
 }
 
+// Byte offset, inside a packed q region, of the 8-byte piece holding segment
+// `seg` (8 values) of block `blk` of row `row`.
+__device__ inline int64_t packed_q_offset(int64_t row, int64_t blk, int seg,
+                                          int64_t NSC) {
+    const int64_t g = row >> 4;
+    const int j = (int)(row & 15);
+    const int64_t sc = blk >> 3;
+    const int bb = (int)(blk & 7);
+    const int c = bb >> 1, h = bb & 1;
+    const int slot = pos_slot(seg);
+    return ((g * NSC + sc) * 4 + c) * kChunkBytes + (slot * 16 + j) * 16 + h * 8;
+}
+
+// Index (in halves) of the scale of block `blk` of row `row` in a packed
+// scale region: [group][chunk][16 rows][2 blocks].
+__device__ inline int64_t packed_d_index(int64_t row, int64_t blk, int64_t NSC) {
+    const int64_t g = row >> 4;
+    const int j = (int)(row & 15);
+    const int64_t c = blk >> 1;
+    return ((g * 4 * NSC + c) * 16 + j) * 2 + (blk & 1);
+}
+
 // ------------------------------------------------------------------------
 // q8_0 quantisation of one 8-value segment by a group of 4 lanes that
 // together hold a 32-value block.  Lanes of the group must be 4 consecutive
@@ -144,6 +166,9 @@ struct Tiling {
 Tiling choose_tiling(const Shape& s);
 // Workspace a split execution needs (0: the shape is not split).
 size_t workspace_bytes(const Shape& s, const Tiling& t);
+// Workspace of the fused pre-quantise + matmul: 64 KB of counters and flags
+// (16 pages of 4 KB), then workspace_bytes().
+constexpr size_t kFusedFlagBytes = 64 * 1024;
 
 enum class Engine { kMfma, kDot4 };
 // workspace: nullptr for the single-workgroup evaluation of the tree, or a
@@ -154,5 +179,13 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
                          int n_slots, const int32_t* batch_index, int n_live,
                          const Shape& s, const Tiling& t, float* Y,
                          void* workspace, hipStream_t st);
+// Pre-quantise X [n_rows][K] into the 16-slot buffer Xq and run the matmul,
+// in one launch (MFMA engine).  workspace: kFusedFlagBytes of counters
+// followed by workspace_bytes() for the split execution, all zero before
+// the first call and left zero by every call.
+hipError_t launch_matmul_fused(const uint8_t* Wq, const float* X, int n_rows,
+                               uint8_t* Xq, const int32_t* batch_index, int n_live,
+                               const Shape& s, const Tiling& t, float* Y,
+                               void* workspace, hipStream_t st);
 
 }  // namespace q8

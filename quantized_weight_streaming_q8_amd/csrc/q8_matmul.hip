@@ -125,6 +125,14 @@ struct MmArgs {
     int CT;               // slot column tiles (16 slots each)
     int64_t xq_gs;        // slot buffer: bytes per 16 slots of the q region
     int64_t xd_gs;        // slot buffer: halves per 16 slots of the scale region
+    // fused pre-quantisation (FUSED kernels only)
+    const float* X;       // fp32 activations [n_rows][K]
+    int n_rows;
+    int P;                // producer workgroups, blockIdx.x < P
+    int n_cons;           // consumer (matmul) workgroups
+    uint32_t* qflag;      // producers that have published their slots
+    uint32_t* qdone;      // consumers past the wait
+    uint32_t* qready;     // kReadyCopies "slots published" flags, kReadyStride apart
 };
 
 // Super-chunk range [lo, hi) of wave slice k of split s (NSC < 2^16, so 32-bit
@@ -192,21 +200,34 @@ struct Chunk {
 // Chunk cg (global chunk index along K) for RG row groups: weights, their
 // scales, and the slot operands (1 KB contiguous for the wave per tile).
 template <int RG, int CT, bool NTW>
-__device__ inline void load_chunk(Chunk<RG, CT>& ch, int cg, const uint8_t* wrow,
-                                  const uint16_t* wdrow, int64_t g_stride_q,
-                                  int64_t g_stride_d, const uint8_t* xa,
-                                  const uint16_t* xdp, int64_t xq_gs, int64_t xd_gs) {
+__device__ inline void load_chunk_w(Chunk<RG, CT>& ch, int cg, const uint8_t* wrow,
+                                    const uint16_t* wdrow, int64_t g_stride_q,
+                                    int64_t g_stride_d) {
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
         const uint8_t* p = wrow + rg * g_stride_q + (int64_t)cg * kChunkBytes;
         ch.w[rg] = NTW ? ld16_v2_nt(p) : ld16_v2(p);
         ch.wd[rg] = ld16(wdrow + rg * g_stride_d + (int64_t)cg * (kChunkDBytes / 2));
     }
+}
+
+template <int RG, int CT>
+__device__ inline void load_chunk_a(Chunk<RG, CT>& ch, int cg, const uint8_t* xa,
+                                    const uint16_t* xdp, int64_t xq_gs, int64_t xd_gs) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
         ch.aq[ct] = ld16_v2(xa + ct * xq_gs + (int64_t)cg * kChunkBytes);
         ch.dx[ct] = *reinterpret_cast<const uint32_t*>(xdp + ct * xd_gs + (int64_t)cg * (kChunkDBytes / 2));
     }
+}
+
+template <int RG, int CT, bool NTW>
+__device__ inline void load_chunk(Chunk<RG, CT>& ch, int cg, const uint8_t* wrow,
+                                  const uint16_t* wdrow, int64_t g_stride_q,
+                                  int64_t g_stride_d, const uint8_t* xa,
+                                  const uint16_t* xdp, int64_t xq_gs, int64_t xd_gs) {
+    load_chunk_w<RG, CT, NTW>(ch, cg, wrow, wdrow, g_stride_q, g_stride_d);
+    load_chunk_a<RG, CT>(ch, cg, xa, xdp, xq_gs, xd_gs);
 }
 
 // Dot one chunk and accumulate: acc[rg][ct][r] is row 4*tq + r of row group
@@ -277,11 +298,101 @@ __device__ inline TileOut tile_out(const MmArgs& a, const int* tok_slot, int o,
     return r;
 }
 
+// ------------------------------------------------------------------------
+// Fused pre-quantisation.  The first P workgroups of a FUSED launch quantise
+// X into the slot buffer (the q8_0 rule of the separate pre-quantiser, same
+// bits), write it with device-coherent stores, wait for the stores to
+// complete and bump qflag; the last of them raises the "published" flags.
+// The matmul workgroups put their first weight chunks in flight, then wait
+// for their flag before their first activation load.  Workgroups are dispatched in index order, so the producers are
+// resident or done before any matmul workgroup waits, and they wait on
+// nothing themselves.  The wait is bounded all the same (kMaxSpins polls):
+// were it ever to run out, the outputs would be wrong (and tests would say
+// so) but the kernel would still finish.  The last matmul workgroup past the
+// wait rearms both counters for the next call.
+// ------------------------------------------------------------------------
+
+constexpr int kMaxSpins = 1 << 22;
+// The "published" signal is polled by one thread per workgroup, each on one
+// of kReadyCopies flags that sit in different memory pages (4 KB apart), so
+// that the polls of a large grid do not all queue on one memory channel.
+constexpr int kReadyCopies = 15;
+constexpr int kReadyStride = 1024;  // uint32 elements (4 KB)
+
+__device__ void produce_slots(const MmArgs& a, int pid) {
+    const int nthreads = blockDim.x;
+    const int64_t bpr = (int64_t)a.NSC * kScBlocks;  // blocks per row, padded
+    const int64_t total = (int64_t)a.n_rows * bpr * 4;  // one lane per 8 values
+    uint8_t* xq = const_cast<uint8_t*>(a.xq);
+    uint16_t* xd = const_cast<uint16_t*>(a.xd);
+    // strides are multiples of 64 and rows hold an even number of blocks, so
+    // a wave always holds whole pairs of blocks (8 lanes) of one row
+    for (int64_t tid = (int64_t)pid * nthreads + threadIdx.x; tid < total;
+         tid += (int64_t)a.P * nthreads) {
+        const int seg = (int)(tid & 3);
+        const int64_t b = tid >> 2;
+        const int64_t blk = b % bpr, row = b / bpr;
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (blk < a.KB) {
+            const float* p = a.X + row * ((int64_t)a.KB * kBlock) + blk * kBlock + seg * 8;
+            const float4 x0 = *reinterpret_cast<const float4*>(p);
+            const float4 x1 = *reinterpret_cast<const float4*>(p + 4);
+            v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+            v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+        }
+        const QuantSeg r = quantize_segment(v);
+        const uint64_t q = (uint64_t)r.lo | ((uint64_t)r.hi << 32);
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(xq + packed_q_offset(row, blk, seg, a.NSC)), q,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the odd block's scale sits next to the even block's: one 4-byte store
+        const uint32_t d_next = __shfl_down((uint32_t)r.d16, 4);
+        if (seg == 0 && (blk & 1) == 0)
+            __hip_atomic_store(reinterpret_cast<uint32_t*>(xd + packed_d_index(row, blk, a.NSC)),
+                               (uint32_t)r.d16 | (d_next << 16), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (threadIdx.x == 0 &&
+        __hip_atomic_fetch_add(a.qflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            (uint32_t)(a.P - 1)) {
+        // the last producer: every slot is published; raise all the flags
+        for (int k = 0; k < kReadyCopies; ++k)
+            __hip_atomic_store(a.qready + k * kReadyStride, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Called by every thread of a matmul workgroup: thread 0 polls the
+// workgroup's flag, the others wait at the barriers.
+__device__ inline void wait_for_slots(const MmArgs& a, int bid) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t* f = a.qready + (bid % kReadyCopies) * kReadyStride;
+        for (int spins = 0; spins < kMaxSpins; ++spins) {
+            if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+            __builtin_amdgcn_s_sleep(4);
+        }
+    }
+    __syncthreads();
+}
+
 // One workgroup per row block (plain: all S*KW waves) or per (row block,
 // split) (SPLIT: KW waves).  LDS: the wave partials red fp32 [waves][RG*256].
-template <int RG, int CT, int D, bool NTW, bool SPLIT>
+// FUSED: the first P workgroups are producers (see above).
+template <int RG, int CT, int D, bool NTW, bool SPLIT, bool FUSED>
 __global__ void __launch_bounds__(512)
 mm_mfma_kernel(MmArgs a) {
+    int bid = (int)blockIdx.x;
+    if (FUSED) {
+        if (bid < a.P) {
+            produce_slots(a, bid);
+            return;
+        }
+        bid -= a.P;
+    }
     static_assert(D == 1 || D == 2 || D == 4, "the ring depth must divide a super-chunk");
     static_assert(RG == 1 || RG == 2, "row groups per wave");
     extern __shared__ __align__(16) float red[];
@@ -292,8 +403,8 @@ mm_mfma_kernel(MmArgs a) {
     const int tq = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int nwaves = SPLIT ? a.KW : a.S * a.KW;
-    const int rb = SPLIT ? (int)(blockIdx.x / a.S) : (int)blockIdx.x;
-    const int split = SPLIT ? (int)(blockIdx.x % a.S) : w / a.KW;
+    const int rb = SPLIT ? bid / a.S : bid;
+    const int split = SPLIT ? bid % a.S : w / a.KW;
     int sc0, sc1;
     slice_range(a.NSC, a.S, a.KW, split, SPLIT ? w : w % a.KW, sc0, sc1);
     const int c_lo = 4 * sc0, c_hi = 4 * sc1;  // this wave's chunks (>= 4)
@@ -326,8 +437,18 @@ mm_mfma_kernel(MmArgs a) {
     if ((int)threadIdx.x < 16 * CT && (int)threadIdx.x < a.n_live) my_slot = a.bidx[threadIdx.x];
 
     Chunk<RG, CT> ring[D];
+    if (FUSED) {
+        // weights first; the slots only once the producers have published them
 #pragma unroll
-    for (int i = 0; i < D; ++i) load_chunk<RG, CT, NTW>(ring[i], c_lo + i, wrow, wdrow, gq, gd, xa, xdp, a.xq_gs, a.xd_gs);
+        for (int i = 0; i < D; ++i) load_chunk_w<RG, CT, NTW>(ring[i], c_lo + i, wrow, wdrow, gq, gd);
+        wait_for_slots(a, bid);
+#pragma unroll
+        for (int i = 0; i < D; ++i) load_chunk_a<RG, CT>(ring[i], c_lo + i, xa, xdp, a.xq_gs, a.xd_gs);
+    } else {
+#pragma unroll
+        for (int i = 0; i < D; ++i)
+            load_chunk<RG, CT, NTW>(ring[i], c_lo + i, wrow, wdrow, gq, gd, xa, xdp, a.xq_gs, a.xd_gs);
+    }
     int c = c_lo;
     for (; c + D < c_hi; c += D) {
 #pragma unroll
@@ -352,6 +473,18 @@ mm_mfma_kernel(MmArgs a) {
                 red[((w * RG + rg) * CT + ct) * 256 + r * 64 + lane] = acc[rg][ct][r];
     if ((int)threadIdx.x < 16 * CT) tok_slot[threadIdx.x] = my_slot;
     __syncthreads();
+    if (FUSED && threadIdx.x == 0) {
+        // every wave of this workgroup is past the wait: the last workgroup
+        // to get here rearms both counters
+        if (__hip_atomic_fetch_add(a.qdone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            (uint32_t)(a.n_cons - 1)) {
+            __hip_atomic_store(a.qflag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.qdone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int k = 0; k < kReadyCopies; ++k)
+                __hip_atomic_store(a.qready + k * kReadyStride, 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 
     const int nthreads = nwaves * 64;
     if (!SPLIT) {
@@ -399,14 +532,23 @@ size_t mfma_lds_bytes(const MmArgs& a, int rg, int ct, bool split) {
 
 int mfma_max_waves(int) { return 8; }  // 512 threads: 256 VGPRs per lane
 
-template <int RG, int CT, int D, bool NTW, bool SPLIT>
-hipError_t launch_mfma(const MmArgs& a, hipStream_t st) {
+template <int RG, int CT, int D, bool NTW, bool SPLIT, bool FUSED = false>
+hipError_t launch_mfma(MmArgs a, hipStream_t st) {
     const int waves = mfma_waves(a, SPLIT);
     const size_t lds = mfma_lds_bytes(a, RG, CT, SPLIT);
     if (lds > kMaxLds || waves > mfma_max_waves(RG) || a.G < RG || a.CT != CT)
         return hipErrorInvalidValue;
-    const unsigned grid = (unsigned)(SPLIT ? (int64_t)a.n_rb * a.S : a.n_rb);
-    hipLaunchKernelGGL((mm_mfma_kernel<RG, CT, D, NTW, SPLIT>), dim3(grid), dim3(64 * waves), lds, st, a);
+    const int64_t cons = SPLIT ? (int64_t)a.n_rb * a.S : a.n_rb;
+    int64_t grid = cons;
+    if (FUSED) {
+        // producers: one lane per 8 activation values, 64*waves lanes each
+        const int64_t lanes = (int64_t)a.n_rows * a.NSC * kScBlocks * 4;
+        a.P = (int)((lanes + 64 * waves - 1) / (64 * waves));
+        a.n_cons = (int)cons;
+        grid += a.P;
+    }
+    hipLaunchKernelGGL((mm_mfma_kernel<RG, CT, D, NTW, SPLIT, FUSED>), dim3((unsigned)grid),
+                       dim3(64 * waves), lds, st, a);
     return hipGetLastError();
 }
 
@@ -651,6 +793,49 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
                               : launch_mfma<2, 1, kRing, true, false>(a, st);
     return split ? launch_mfma<1, 1, kRing, true, true>(a, st)
                  : launch_mfma<1, 1, kRing, true, false>(a, st);
+}
+
+hipError_t launch_matmul_fused(const uint8_t* Wq, const float* X, int n_rows,
+                               uint8_t* Xq, const int32_t* batch_index, int n_live,
+                               const Shape& s, const Tiling& t, float* Y,
+                               void* workspace, hipStream_t st) {
+    MmArgs a;
+    a.CT = 1;
+    a.wq = Wq;
+    a.wd = reinterpret_cast<const uint16_t*>(Wq + s.q_bytes);
+    a.xq = Xq;
+    a.xd = reinterpret_cast<const uint16_t*>(Xq + s.act_q_bytes);
+    a.xq_gs = s.act_q_bytes;
+    a.xd_gs = s.NSC * 4 * (kChunkDBytes / 2);
+    a.bidx = batch_index;
+    a.Y = Y;
+    a.N = s.N;
+    a.G = s.G;
+    a.KB = (int)s.KB;
+    a.NSC = (int)s.NSC;
+    a.n_live = n_live;
+    a.S = t.splits;
+    a.KW = t.kw;
+    a.X = X;
+    a.n_rows = n_rows;
+    a.qflag = static_cast<uint32_t*>(workspace);
+    a.qdone = a.qflag + 32;            // its own 128-byte line
+    a.qready = a.qflag + kReadyStride;  // pages 1..kReadyCopies
+    if (a.S * a.KW > a.NSC) return hipErrorInvalidValue;
+    const bool split = t.splits > 1;
+    const int rg = launch_rg(s, t, split);
+    a.n_rb = (int)((s.G + rg - 1) / rg);
+    a.counters = nullptr;
+    a.part = nullptr;
+    if (split) {
+        uint8_t* ws = static_cast<uint8_t*>(workspace) + kFusedFlagBytes;
+        a.counters = reinterpret_cast<uint32_t*>(ws);
+        a.part = reinterpret_cast<float*>(ws + align_up((int64_t)a.n_rb * 4, 256));
+    }
+    if (rg == 2) return split ? launch_mfma<2, 1, kRing, true, true, true>(a, st)
+                              : launch_mfma<2, 1, kRing, true, false, true>(a, st);
+    return split ? launch_mfma<1, 1, kRing, true, true, true>(a, st)
+                 : launch_mfma<1, 1, kRing, true, false, true>(a, st);
 }
 
 }  // namespace q8

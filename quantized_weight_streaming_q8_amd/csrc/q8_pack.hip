@@ -42,28 +42,6 @@ __device__ inline void load8(const float* p, float v[8]) {
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// Byte offset, inside the packed q region, of the 8-byte piece holding
-// segment `seg` of block `blk` of row `row`.
-__device__ inline int64_t packed_q_offset(int64_t row, int64_t blk, int seg,
-                                          int64_t NSC) {
-    const int64_t g = row >> 4;
-    const int j = (int)(row & 15);
-    const int64_t sc = blk >> 3;
-    const int bb = (int)(blk & 7);
-    const int c = bb >> 1, h = bb & 1;
-    const int slot = pos_slot(seg);
-    return ((g * NSC + sc) * 4 + c) * kChunkBytes + (slot * 16 + j) * 16 + h * 8;
-}
-
-// Index (in halves) of the scale of block `blk` of row `row` in the packed
-// scale region: [group][chunk][16 rows][2 blocks].
-__device__ inline int64_t packed_d_index(int64_t row, int64_t blk, int64_t NSC) {
-    const int64_t g = row >> 4;
-    const int j = (int)(row & 15);
-    const int64_t c = blk >> 1;
-    return ((g * 4 * NSC + c) * 16 + j) * 2 + (blk & 1);
-}
-
 __global__ void __launch_bounds__(kThreads)
 pack_weights_kernel(const float* __restrict__ W, int64_t N, int64_t K,
                     int64_t KB, int64_t NSC, int64_t total,

@@ -29,7 +29,7 @@ def test_header_declares_the_abi():
     names = header_functions()
     for core in ("q8_pack_weights", "q8_quantize_acts", "q8_matmul_narrow"):
         assert core in names
-    assert len(names) == 15, names
+    assert len(names) == 17, names
 
 
 def test_every_declared_symbol_is_exported(q8):
@@ -197,3 +197,28 @@ def test_multi_column_calls_reject_invalid_arguments(q8):
     assert lib.q8_matmul_multi(P, P, 64, P + 2, 4, 64, 64, P, None) == bad
     assert lib.q8_matmul_multi(P, P, 64, P, 4, 64, 64, P + 1, None) == bad
     assert lib.q8_quantize_acts_n(P + 4, 4, 64, P, 64, None) == bad
+
+
+def test_fused_workspace_sizes(q8):
+    for N, K in ((5120, 5120), (5120, 17408), (151936, 5120), (16, 32)):
+        assert q8.q8_matmul_fused_workspace_bytes(N, K) == 65536 + q8.q8_matmul_workspace_bytes(N, K)
+    assert q8.q8_matmul_fused_workspace_bytes(0, 5120) == 0
+
+
+def test_fused_call_rejects_invalid_arguments(q8):
+    lib = q8.library()
+    bad = q8.Q8_ERR_INVALID_ARG
+    need = q8.q8_matmul_fused_workspace_bytes(64, 64)
+    ok = (P, P, 4, P, P, 4, 64, 64, P, P, need, None)
+    def call(**kw):
+        args = list(ok)
+        for i, v in kw.items():
+            args[int(i[1:])] = v
+        return lib.q8_matmul_narrow_fused(*args)
+    assert call(a2=0) == bad and call(a2=17) == bad          # n_rows
+    assert call(a5=0) == bad and call(a5=17) == bad          # n_live
+    assert call(a7=48) == bad                                # K % 32
+    assert call(a0=None) == bad and call(a1=P + 4) == bad    # Wq null, X misaligned
+    assert call(a3=P + 8) == bad and call(a4=P + 2) == bad   # Xq, batch_index misaligned
+    assert call(a9=None) == bad and call(a9=P + 16) == bad   # workspace missing, misaligned
+    assert call(a10=need - 1) == bad                         # workspace too small
