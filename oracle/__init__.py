@@ -79,6 +79,8 @@ class Oracle:
         lib.q8o_block_dots.argtypes = [vp, i64, i64, vp, i32, vp, i32, vp,
                                        i64, vp]
         lib.q8o_block_dots.restype = i32
+        lib.q8o_rope.argtypes = [vp, i64, i64, vp, i64, i64, ctypes.c_double, vp, vp]
+        lib.q8o_rope.restype = i32
         lib.q8o_num_threads.argtypes = []
         lib.q8o_num_threads.restype = i32
         lib.q8o_set_num_threads.argtypes = [i32]
@@ -169,6 +171,27 @@ class Oracle:
         return S
 
     # ------------------------------------------------------------- threads
+    def rope(self, Y, pos, n_heads: int, head_dim: int, base: float):
+        """Oracle pos-vector RoPE.
+
+        Y float32 [n_rows][row_stride]: heads 0..n_heads-1 in the first
+        n_heads*head_dim columns; pos int32 [n_rows], one position per row.
+        Returns ``(out, mag)``, float64 [n_rows][n_heads*head_dim]: the
+        rotated values and |a| + |b| of each value's pair.
+        """
+        Y = _c(Y, np.float32)
+        pos = _c(pos, np.int32).reshape(-1)
+        n_rows, stride = Y.shape
+        if pos.size != n_rows:
+            raise ValueError("one position per row")
+        out = np.empty((n_rows, n_heads * head_dim), dtype=np.float64)
+        mag = np.empty_like(out)
+        rc = self._lib.q8o_rope(_ptr(Y), n_rows, stride, _ptr(pos), n_heads, head_dim,
+                                float(base), _ptr(out), _ptr(mag))
+        if rc:
+            raise ValueError("invalid rope arguments")
+        return out, mag
+
     def num_threads(self) -> int:
         return int(self._lib.q8o_num_threads())
 
@@ -207,6 +230,10 @@ def matmul(qw, dw, qx, dx, batch_index, rows=None):
 
 def block_dots(qw, qx, batch_index, rows=None):
     return get().block_dots(qw, qx, batch_index, rows)
+
+
+def rope(Y, pos, n_heads: int, head_dim: int, base: float):
+    return get().rope(Y, pos, n_heads, head_dim, base)
 
 
 def num_threads() -> int:

@@ -32,6 +32,9 @@
  *    ascending block order.  The oracle also returns A = sum_b |term|, the
  *    scale of the summation error any fp32 implementation may make.
  *
+ *  - Pos-vector rotary position embedding (below, q8o_rope): the consumer
+ *    of the QKV projection in a batched decode step.
+ *
  * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC.
  * OpenMP only splits independent output rows; each output is computed by one
  * thread in the order written below.
@@ -269,6 +272,49 @@ int q8o_block_dots(const int8_t* qw, int64_t N, int64_t K, const int8_t* qx,
 }
 
 /* Number of OpenMP threads a parallel region here would use. */
+/* ------------------------------------------------------------------------
+ * Pos-vector rotary position embedding.  "Batched decode: co-decode N live
+ * sessions in one GPU pass" (antirez/ds4 PR #530), commit "CUDA: add
+ * pos-vector RoPE tail variants": in a batched decode step each row (token)
+ * sits at its own position, so the rotation takes a small array of
+ * positions indexed by row, and every row must come out exactly as a
+ * single-token launch would make it.  The pages name the operation, not its
+ * formula; this is the plain rotary embedding with the "rotate half"
+ * pairing of the Qwen family: in each head of head_dim values, values i and
+ * i + head_dim/2 (i < head_dim/2) turn by the angle
+ *     theta = pos * base^(-2i/head_dim)
+ *     out_i          = a cos(theta) - b sin(theta)
+ *     out_{i+half}   = a sin(theta) + b cos(theta)
+ * with a, b the two inputs.  Everything in double; mag receives |a| + |b| of
+ * each value's pair, the scale of the rounding error of any implementation.
+ * Rows are n_rows rows of Y, row_stride floats apart; heads 0..n_heads-1
+ * occupy the first n_heads*head_dim columns.  out and mag are
+ * [n_rows][n_heads*head_dim].  Returns 1 for an invalid argument.
+ * ------------------------------------------------------------------------ */
+int q8o_rope(const float* Y, int64_t n_rows, int64_t row_stride, const int32_t* pos,
+             int64_t n_heads, int64_t head_dim, double base, double* out, double* mag) {
+    if (n_rows < 1 || n_heads < 1 || head_dim < 2 || (head_dim & 1) ||
+        n_heads * head_dim > row_stride || !(base > 0.0))
+        return 1;
+    const int64_t half = head_dim / 2, width = n_heads * head_dim;
+    for (int64_t t = 0; t < n_rows; ++t) {
+        for (int64_t h = 0; h < n_heads; ++h) {
+            for (int64_t i = 0; i < half; ++i) {
+                const double theta = (double)pos[t] * pow(base, -2.0 * (double)i / (double)head_dim);
+                const double c = cos(theta), sn = sin(theta);
+                const double a = Y[t * row_stride + h * head_dim + i];
+                const double b = Y[t * row_stride + h * head_dim + i + half];
+                double* o = out + t * width + h * head_dim;
+                double* m = mag + t * width + h * head_dim;
+                o[i] = a * c - b * sn;
+                o[i + half] = a * sn + b * c;
+                m[i] = m[i + half] = fabs(a) + fabs(b);
+            }
+        }
+    }
+    return 0;
+}
+
 int q8o_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

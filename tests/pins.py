@@ -413,3 +413,82 @@ def pin_quant_invariants_default(orc):
 
 
 FAST_PINS.append(pin_quant_invariants_default)
+
+
+# --------------------------------------------------------------------------
+# pos-vector RoPE
+# --------------------------------------------------------------------------
+
+def load_rope_closed_forms(path: str | None = None):
+    path = path or os.path.join(GOLDEN, "rope_closed_forms.txt")
+    cases = []
+    with open(path) as fh:
+        for raw in fh:
+            line = raw.split("#", 1)[0].strip()
+            if not line:
+                continue
+            head, xs, ys = (p.strip() for p in line.split("|"))
+            base, d, pos = head.split()
+            cases.append((float(base), int(d), int(pos),
+                          np.array([float(v) for v in xs.split()], dtype=np.float32),
+                          np.array([float(v) for v in ys.split()], dtype=np.float64)))
+    return cases
+
+
+def pin_rope_closed_forms(orc):
+    """Hand-derived rotations: which values pair up, by what angle, which
+    signs, and the row's own position (rows of one call carry different
+    positions)."""
+    cases = load_rope_closed_forms()
+    for base, d, pos, x, y in cases:
+        out, mag = orc.rope(x[None, :], np.array([pos], dtype=np.int32), 1, d, base)
+        assert np.allclose(out[0], y, rtol=0, atol=4e-16), (base, d, pos)
+        half = d // 2
+        assert np.allclose(mag[0, :half], np.abs(x[:half]) + np.abs(x[half:])), (base, d, pos)
+    # several rows of one call, each with its own position
+    groups = {}
+    for c in cases:
+        groups.setdefault((c[0], c[1]), []).append(c)
+    mixed = 0
+    for (base, d), same in groups.items():
+        if len(same) < 2:
+            continue
+        mixed += len({c[2] for c in same}) > 1
+        Y = np.stack([c[3] for c in same])
+        out, _ = orc.rope(Y, np.array([c[2] for c in same], dtype=np.int32), 1, d, base)
+        for r, c in enumerate(same):
+            assert np.allclose(out[r], c[4], rtol=0, atol=4e-16), (base, d, r)
+    assert mixed, "no call mixes positions"
+
+
+def pin_rope_group(orc, seed: int = 23):
+    """Rotation-group identities on random heads: the pair norms are kept,
+    turning back by -pos restores the input, two turns add their positions,
+    and the dot product of two rotated heads depends only on the position
+    difference (the relative-position property)."""
+    rng = np.random.default_rng(seed)
+    H, d, base = 3, 16, 10000.0
+    x = rng.standard_normal((4, H * d + 5), dtype=np.float32)  # extra columns are not heads
+    pos = np.array([0, 5, 123, 40000], dtype=np.int32)
+    out, mag = orc.rope(x, pos, H, d, base)
+    half = d // 2
+    xa = x[:, :H * d].reshape(4, H, 2, half).astype(np.float64)
+    oa = out.reshape(4, H, 2, half)
+    assert np.allclose(np.hypot(oa[:, :, 0], oa[:, :, 1]), np.hypot(xa[:, :, 0], xa[:, :, 1]),
+                       rtol=1e-12, atol=0)
+    back, _ = orc.rope(out.astype(np.float32), -pos, H, d, base)
+    assert np.allclose(back, x[:, :H * d], rtol=0, atol=1e-6 * np.max(mag))
+    p1, p2 = np.array([3, 7, 11, 2], np.int32), np.array([5, 1, 100, 9], np.int32)
+    once, _ = orc.rope(x, p1 + p2, H, d, base)
+    twice, _ = orc.rope(orc.rope(x, p1, H, d, base)[0].astype(np.float32), p2, H, d, base)
+    assert np.allclose(once, twice, rtol=0, atol=1e-6 * np.max(mag))
+    q, k = x[0:1, :H * d], x[1:2, :H * d]
+    def dots(m, n):
+        rq, _ = orc.rope(q, np.array([m], np.int32), H, d, base)
+        rk, _ = orc.rope(k, np.array([n], np.int32), H, d, base)
+        return (rq.reshape(H, d) * rk.reshape(H, d)).sum(axis=1)
+    assert np.allclose(dots(10, 3), dots(1007, 1000), rtol=1e-9, atol=1e-12)
+    assert not np.allclose(dots(10, 3), dots(10, 4), rtol=1e-6)
+
+
+FAST_PINS += [pin_rope_closed_forms, pin_rope_group]

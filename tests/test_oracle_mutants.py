@@ -48,6 +48,14 @@ MUTANTS = {
     "abs_sum_signed": ("a += fabs(term);", "a += term;"),
     "first_block_skipped": ("for (int64_t b = 0; b < KB; ++b) {\n                const int32_t S",
                             "for (int64_t b = 1; b < KB; ++b) {\n                const int32_t S"),
+    # pos-vector RoPE
+    "rope_interleaved_pairs": ("const double b = Y[t * row_stride + h * head_dim + i + half];",
+                               "const double b = Y[t * row_stride + h * head_dim + (2 * i + 1) % head_dim];"),
+    "rope_exponent_halved": ("pow(base, -2.0 * (double)i / (double)head_dim)",
+                             "pow(base, -(double)i / (double)head_dim)"),
+    "rope_sign": ("o[i] = a * c - b * sn;", "o[i] = a * c + b * sn;"),
+    "rope_first_row_position": ("(double)pos[t] * pow(", "(double)pos[0] * pow("),
+    "rope_position_off_by_one": ("(double)pos[t] * pow(", "(double)(pos[t] + 1) * pow("),
     "block_dots_wrong_row": ("? 0\n                             : block_dot(qw + n * K",
                              "? 0\n                             : block_dot(qw + (n ? n - 1 : n) * K"),
 }
