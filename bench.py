@@ -373,6 +373,30 @@ def multi_columns(layer: Layer, widths, launches: int) -> dict:
     return out
 
 
+# ------------------------------------------------------ pos-vector RoPE
+
+ROPE_HEADS, ROPE_HEAD_DIM, ROPE_BASE = 48, 128, 1e6  # Qwen3-14B: 40 query + 8 key heads
+
+
+def rope_after_qkv(layer: Layer, n_live: int, launches: int = 100):
+    """The pos-vector RoPE on the QKV matmul's output rows (the query and key
+    heads of the Qwen3-14B layer, one position per live token): average
+    launch duration and algorithmic GB/s (each rotated value read and written
+    once in fp32, plus the positions)."""
+    import torch
+    q8 = layer.q8
+    i = [k for k, m in enumerate(layer.mats) if m.name == "qkv"]
+    if not i:
+        return None
+    m = layer.mats[i[0]]
+    pos = torch.arange(1000, 1000 + n_live, dtype=torch.int32, device="cuda") * 37
+    us = graph_avg_us(lambda c: q8.q8_rope_multi(layer.Y[i[0]], n_live, m.N, pos, ROPE_HEADS,
+                                                 ROPE_HEAD_DIM, ROPE_BASE), launches)
+    nbytes = 2 * 4 * n_live * ROPE_HEADS * ROPE_HEAD_DIM + 4 * n_live
+    return {"us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1), "rows": n_live,
+            "heads": ROPE_HEADS, "head_dim": ROPE_HEAD_DIM, "base": ROPE_BASE}
+
+
 # ------------------------------------------------------- engine A/B
 
 def engine_ab(layer: Layer, n_values, launches: int) -> dict:
@@ -632,6 +656,9 @@ def main(argv=None) -> int:
 
     multi = multi_columns(layer, (16, 32, 48, 64), max(16, 4 * layer.copies)) \
         if args.multi else None
+    rope = rope_after_qkv(layer, args.n_live)
+    if rope:
+        print(f"# pos-vector RoPE on the QKV rows: {rope['us']} us", file=sys.stderr, flush=True)
     copy_gbs = copy_ceiling_gbs()
     cpu = cpu_baseline(args.workload, args.n_live, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
@@ -674,6 +701,7 @@ def main(argv=None) -> int:
         "sweep": sweep,
         "roofline": roofline,
         "multi_columns": multi,
+        "rope_after_qkv": rope,
         "copy_ceiling_GBps": round(copy_gbs, 1),
         "cpu_baseline": cpu,
     }

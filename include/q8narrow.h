@@ -227,6 +227,30 @@ q8_status q8_matmul_multi(const void* Wq, const void* Xq, int n_slots,
                           const int32_t* batch_index, int n_live, int64_t N,
                           int64_t K, float* Y, hipStream_t stream);
 
+/* ------------------------------------------------------ pos-vector RoPE */
+
+/* Rotary position embedding with one position per row, in place, for the
+ * rows a batched QKV projection produces.  "Batched decode: co-decode N
+ * live sessions in one GPU pass" (antirez/ds4 PR #530), commit "CUDA: add
+ * pos-vector RoPE tail variants": each row (token) has its own position,
+ * read from a small per-row array, and each row's result is bitwise the one
+ * a single-row call would give.
+ *
+ * Y: fp32 rows, n_rows of them, row_stride floats apart (e.g. the [n_live][N]
+ * output of q8_matmul_narrow, row_stride = N); the first n_heads * head_dim
+ * columns are the heads to rotate (e.g. the query and key heads), the rest
+ * are left untouched.  pos: int32 [n_rows] device array.  In each head,
+ * values i and i + head_dim/2 (i < head_dim/2) are rotated by the angle
+ * pos[t] * base^(-2i/head_dim) (the rotate-half pairing); the angle, its
+ * sine and cosine and the rotation are computed in double and rounded once
+ * to fp32.
+ *
+ * 1 <= n_rows <= Q8_MAX_COLUMNS; n_heads >= 1; head_dim even, 2..1024;
+ * n_heads * head_dim <= row_stride; 1 < base < 1e30; Y and pos 4-byte
+ * aligned. */
+q8_status q8_rope_multi(float* Y, int n_rows, int64_t row_stride, const int32_t* pos,
+                        int n_heads, int head_dim, double base, hipStream_t stream);
+
 /* ---------------------------------------------------------------- misc */
 
 /* 1 if the current HIP device is gfx950, 0 if not or if none is usable. */

@@ -51,6 +51,7 @@ _SIGNATURES = {
     "q8_act_buffer_bytes_n": ([_i64, _i32], ctypes.c_size_t),
     "q8_quantize_acts_n": ([_vp, _i32, _i64, _vp, _i32, _vp], _i32),
     "q8_matmul_multi": ([_vp, _vp, _i32, _vp, _i32, _i64, _i64, _vp, _vp], _i32),
+    "q8_rope_multi": ([_vp, _i32, _i64, _vp, _i32, _i32, ctypes.c_double, _vp], _i32),
     "q8_device_supported": ([], _i32),
     "q8_status_str": ([_i32], ctypes.c_char_p),
 }
@@ -201,6 +202,12 @@ def q8_matmul_multi(Wq, Xq, n_slots: int, batch_index, n_live: int, N: int, K: i
                     stream=None) -> None:
     _check(_lib.q8_matmul_multi(_ptr(Wq), _ptr(Xq), n_slots, _ptr(batch_index), n_live, N, K,
                                 _ptr(Y), _stream(stream)), "q8_matmul_multi")
+
+
+def q8_rope_multi(Y, n_rows: int, row_stride: int, pos, n_heads: int, head_dim: int,
+                  base: float, stream=None) -> None:
+    _check(_lib.q8_rope_multi(_ptr(Y), n_rows, row_stride, _ptr(pos), n_heads, head_dim,
+                              float(base), _stream(stream)), "q8_rope_multi")
 
 
 def q8_device_supported() -> bool:

@@ -201,6 +201,18 @@ q8_status q8_matmul_multi(const void* Wq, const void* Xq, int n_slots,
                                       n_live, s, t, Y, nullptr, stream));
 }
 
+q8_status q8_rope_multi(float* Y, int n_rows, int64_t row_stride, const int32_t* pos,
+                        int n_heads, int head_dim, double base, hipStream_t stream) {
+    if (n_rows < 1 || n_rows > Q8_MAX_COLUMNS || n_heads < 1 || head_dim < 2 ||
+        head_dim % 2 != 0 || head_dim > 1024 || row_stride < (int64_t)n_heads * head_dim ||
+        row_stride > (int64_t(1) << 40) / n_rows || !(base > 1.0) || !(base < 1e30) ||
+        !aligned(Y, 4) || !aligned(pos, 4))
+        return Q8_ERR_INVALID_ARG;
+    if (!current_device_ok()) return Q8_ERR_UNSUPPORTED;
+    return from_hip(q8::launch_rope_multi(Y, n_rows, row_stride, pos, n_heads, head_dim, base,
+                                          stream));
+}
+
 int q8_device_supported(void) { return current_device_ok(); }
 
 const char* q8_status_str(q8_status status) {

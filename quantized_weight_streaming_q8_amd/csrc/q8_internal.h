@@ -164,6 +164,11 @@ struct Tiling {
     bool nt_weights;  // non-temporal loads for the weight stream
 };
 Tiling choose_tiling(const Shape& s);
+
+// Pos-vector RoPE in place on rows of Y (see q8_rope.hip).  Arguments are
+// validated by the caller.
+hipError_t launch_rope_multi(float* Y, int n_rows, int64_t row_stride, const int32_t* pos,
+                             int n_heads, int head_dim, double base, hipStream_t st);
 // Workspace a split execution needs (0: the shape is not split).
 size_t workspace_bytes(const Shape& s, const Tiling& t);
 // Workspace of the fused pre-quantise + matmul: 64 KB of counters and flags

@@ -29,7 +29,7 @@ def test_header_declares_the_abi():
     names = header_functions()
     for core in ("q8_pack_weights", "q8_quantize_acts", "q8_matmul_narrow"):
         assert core in names
-    assert len(names) == 17, names
+    assert len(names) == 18, names
 
 
 def test_every_declared_symbol_is_exported(q8):
@@ -222,3 +222,20 @@ def test_fused_call_rejects_invalid_arguments(q8):
     assert call(a3=P + 8) == bad and call(a4=P + 2) == bad   # Xq, batch_index misaligned
     assert call(a9=None) == bad and call(a9=P + 16) == bad   # workspace missing, misaligned
     assert call(a10=need - 1) == bad                         # workspace too small
+
+
+def test_rope_rejects_invalid_arguments(q8):
+    lib = q8.library()
+    bad = q8.Q8_ERR_INVALID_ARG
+    ok = [P, 4, 7168, P, 48, 128, 1e6, None]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return lib.q8_rope_multi(*a)
+    assert call(1, 0) == bad and call(1, 65) == bad          # n_rows
+    assert call(2, 48 * 128 - 1) == bad                      # heads do not fit the row
+    assert call(4, 0) == bad                                 # n_heads
+    assert call(5, 127) == bad and call(5, 0) == bad and call(5, 2048) == bad  # head_dim
+    assert call(6, 1.0) == bad and call(6, float("nan")) == bad and call(6, -5.0) == bad
+    assert call(0, None) == bad and call(0, P + 2) == bad    # Y null, misaligned
+    assert call(3, None) == bad and call(3, P + 1) == bad    # pos null, misaligned
