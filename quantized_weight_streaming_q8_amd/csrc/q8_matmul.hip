@@ -513,13 +513,45 @@ mm_mfma_kernel(MmArgs a) {
                                            __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(a.S - 1);
     __syncthreads();
     if (!last_flag) return;
-    // the last split to arrive: level 2 in split order, then rearm the counter
-    for (int o = threadIdx.x; o < E; o += nthreads) {
-        const TileOut to = tile_out<RG, CT>(a, tok_slot, o, gbase, gskip);
-        if (!to.store) continue;
-        float y = coherent_load(a.part + (int64_t)rb * E + to.e);
-        for (int s = 1; s < a.S; ++s) y += coherent_load(a.part + ((int64_t)s * a.n_rb + rb) * E + to.e);
-        a.Y[(int64_t)to.t * a.N + to.n] = to.bad ? __builtin_nanf("") : y;
+    // the last split to arrive: level 2 in split order, then rearm the counter.
+    // A thread's partials (up to kCombineOut outputs x kCombineSplits splits)
+    // are all loaded before any is added, so their memory round trips
+    // overlap instead of queueing one output after the other.
+    constexpr int kCombineOut = 4, kCombineSplits = 8;
+    if (a.S <= kCombineSplits) {
+        for (int o0 = threadIdx.x; o0 < E; o0 += kCombineOut * nthreads) {
+            TileOut to[kCombineOut];
+            float p[kCombineOut][kCombineSplits];
+#pragma unroll
+            for (int k = 0; k < kCombineOut; ++k) {
+                const int o = o0 + k * nthreads;
+                to[k] = tile_out<RG, CT>(a, tok_slot, o < E ? o : 0, gbase, gskip);
+                to[k].store = to[k].store && o < E;
+#pragma unroll
+                for (int s = 0; s < kCombineSplits; ++s)
+                    p[k][s] = (to[k].store && s < a.S)
+                                  ? coherent_load(a.part + ((int64_t)s * a.n_rb + rb) * E + to[k].e)
+                                  : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < kCombineOut; ++k) {
+                if (!to[k].store) continue;
+                float y = p[k][0];
+#pragma unroll
+                for (int s = 1; s < kCombineSplits; ++s)
+                    if (s < a.S) y += p[k][s];
+                a.Y[(int64_t)to[k].t * a.N + to[k].n] = to[k].bad ? __builtin_nanf("") : y;
+            }
+        }
+    } else {
+        for (int o = threadIdx.x; o < E; o += nthreads) {
+            const TileOut to = tile_out<RG, CT>(a, tok_slot, o, gbase, gskip);
+            if (!to.store) continue;
+            float y = coherent_load(a.part + (int64_t)rb * E + to.e);
+            for (int s = 1; s < a.S; ++s)
+                y += coherent_load(a.part + ((int64_t)s * a.n_rb + rb) * E + to.e);
+            a.Y[(int64_t)to.t * a.N + to.n] = to.bad ? __builtin_nanf("") : y;
+        }
     }
     if (threadIdx.x == 0) __hip_atomic_store(a.counters + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
