@@ -51,6 +51,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 #ifdef Q8_TUNING
 #include <cstdlib>
 #endif
@@ -189,73 +190,153 @@ __device__ inline v2i64 ld16_v2_nt(const void* p) {
 }
 
 // Operands of one chunk for RG row groups and CT column tiles of 16 slots.
+// The scales are not part of it: they come once per super-chunk (see
+// load_scales).
 template <int RG, int CT>
 struct Chunk {
     v2i64 w[RG];       // weights: this lane's A operands of blocks 2c, 2c+1
-    uint4 wd[RG];      // rows 4*tq .. 4*tq+3: binary16 scales of blocks 2c, 2c+1
     v2i64 aq[CT];      // slot 16*ct + (lane & 15): B operands of blocks 2c, 2c+1
-    uint32_t dx[CT];   // the same slot: binary16 scales of blocks 2c, 2c+1
 };
 
-// Chunk cg (global chunk index along K) for RG row groups: weights, their
-// scales, and the slot operands (1 KB contiguous for the wave per tile).
+// Chunk cg (global chunk index along K) for RG row groups: the weights (1 KB
+// contiguous for the wave per row group).
 template <int RG, int CT, bool NTW>
 __device__ inline void load_chunk_w(Chunk<RG, CT>& ch, int cg, const uint8_t* wrow,
-                                    const uint16_t* wdrow, int64_t g_stride_q,
-                                    int64_t g_stride_d) {
+                                    int64_t g_stride_q) {
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
         const uint8_t* p = wrow + rg * g_stride_q + (int64_t)cg * kChunkBytes;
         ch.w[rg] = NTW ? ld16_v2_nt(p) : ld16_v2(p);
-        ch.wd[rg] = ld16(wdrow + rg * g_stride_d + (int64_t)cg * (kChunkDBytes / 2));
     }
 }
 
-template <int RG, int CT>
-__device__ inline void load_chunk_a(Chunk<RG, CT>& ch, int cg, const uint8_t* xa,
-                                    const uint16_t* xdp, int64_t xq_gs, int64_t xd_gs) {
+// Weight scales of super-chunk sc for RG row groups: its 4 chunks x 16 rows
+// x 2 blocks are 64 dwords, 256 contiguous bytes, and each lane loads one of
+// them, so the wave reads every scale once.  Lane (tq, j) = (lane >> 4,
+// lane & 15) takes row 4*tq + (j & 3) of chunk j >> 2; the lanes of row tq of
+// the wave between them hold everything lanes tq*16 .. tq*16+15 need (rows
+// 4*tq .. 4*tq+3), and chunk_scale hands each its value with a row broadcast.
+// wsrow already points at this lane's dword in super-chunk 0.
+template <int RG>
+__device__ inline void load_scales(uint32_t ws[RG], int sc, const uint16_t* wsrow,
+                                   int64_t g_stride_d) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-        ch.aq[ct] = ld16_v2(xa + ct * xq_gs + (int64_t)cg * kChunkBytes);
-        ch.dx[ct] = *reinterpret_cast<const uint32_t*>(xdp + ct * xd_gs + (int64_t)cg * (kChunkDBytes / 2));
-    }
+    for (int rg = 0; rg < RG; ++rg)
+        ws[rg] = *reinterpret_cast<const uint32_t*>(wsrow + rg * g_stride_d +
+                                                    (int64_t)sc * (4 * kChunkDBytes / 2));
+}
+
+// Row 4*tq + r, chunk C of the super-chunk: the dword of lane tq*16 + 4*C + r
+// (DPP row_newbcast: every lane of a 16-lane row reads lane 4*C + r of it).
+template <int C, int R>
+__device__ inline uint32_t chunk_scale(uint32_t ws) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)ws, 0x150 + 4 * C + R, 0xf, 0xf, true);
+}
+
+template <int RG, int CT>
+__device__ inline void load_chunk_a(Chunk<RG, CT>& ch, int cg, const uint8_t* xa, int64_t xq_gs) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) ch.aq[ct] = ld16_v2(xa + ct * xq_gs + (int64_t)cg * kChunkBytes);
 }
 
 template <int RG, int CT, bool NTW>
 __device__ inline void load_chunk(Chunk<RG, CT>& ch, int cg, const uint8_t* wrow,
-                                  const uint16_t* wdrow, int64_t g_stride_q,
-                                  int64_t g_stride_d, const uint8_t* xa,
-                                  const uint16_t* xdp, int64_t xq_gs, int64_t xd_gs) {
-    load_chunk_w<RG, CT, NTW>(ch, cg, wrow, wdrow, g_stride_q, g_stride_d);
-    load_chunk_a<RG, CT>(ch, cg, xa, xdp, xq_gs, xd_gs);
+                                  int64_t g_stride_q, const uint8_t* xa, int64_t xq_gs) {
+    load_chunk_w<RG, CT, NTW>(ch, cg, wrow, g_stride_q);
+    load_chunk_a<RG, CT>(ch, cg, xa, xq_gs);
 }
 
-// Dot one chunk and accumulate: acc[rg][ct][r] is row 4*tq + r of row group
-// rg for slot 16*ct + (lane & 15).  Blocks past K (the padding of the last
-// super-chunk) hold zero codes and zero scales on both sides: their term is
-// fma(0, +0, acc), which returns acc unchanged (acc starts at +0 and no term
-// can make it -0), so they need no test.
-template <int RG, int CT>
-__device__ inline void mfma_chunk(const Chunk<RG, CT>& ch, float acc[RG][CT][4]) {
+// Slot scales of super-chunk sc for CT column tiles: 4 chunks x 16 slots x 2
+// blocks, 64 dwords, one per lane: lane l takes chunk l >> 4 of slot l & 15,
+// which is the dword l of the super-chunk.  xsrow points at this lane's dword
+// in super-chunk 0 of tile 0.
+template <int CT>
+__device__ inline void load_slot_scales(uint32_t xs[CT], int sc, const uint16_t* xsrow,
+                                        int64_t xd_gs) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+        xs[ct] = *reinterpret_cast<const uint32_t*>(xsrow + ct * xd_gs +
+                                                    (int64_t)sc * (4 * kChunkDBytes / 2));
+}
+
+// Lane l needs chunk c's dword of its slot l & 15, which lane 16*c + (l & 15)
+// holds: row c of the wave copied to all four 16-lane rows.  A 32-lane swap
+// of the wave with itself gives rows 0101 and 2323, a 16-lane swap of either
+// with itself then rows 0000 and 1111 (2222 and 3333).  One column tile
+// keeps all four copies for the super-chunk; wider tiles, short of
+// registers, make each chunk's copy when it is used.
+template <int CT>
+struct SlotScales {
+    uint32_t xb[CT][CT == 1 ? 4 : 1];
+
+    __device__ inline void prepare(const uint32_t xs[CT]) {
+        if constexpr (CT == 1) {
+            const auto p = __builtin_amdgcn_permlane32_swap(xs[0], xs[0], false, false);
+            const auto q = __builtin_amdgcn_permlane16_swap(p[0], p[0], false, false);
+            const auto r = __builtin_amdgcn_permlane16_swap(p[1], p[1], false, false);
+            xb[0][0] = q[0];
+            xb[0][1] = q[1];
+            xb[0][2] = r[0];
+            xb[0][3] = r[1];
+        } else {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) xb[ct][0] = xs[ct];
+        }
+    }
+
+    template <int C>
+    __device__ inline uint32_t get(int ct) const {
+        if constexpr (CT == 1) {
+            return xb[0][C];
+        } else {
+            const auto p = __builtin_amdgcn_permlane32_swap(xb[ct][0], xb[ct][0], false, false);
+            const uint32_t h = p[C >> 1];
+            return __builtin_amdgcn_permlane16_swap(h, h, false, false)[C & 1];
+        }
+    }
+};
+
+// Dot chunk C of a super-chunk and accumulate: acc[rg][ct][r] is row
+// 4*tq + r of row group rg for slot 16*ct + (lane & 15); ws[rg] holds the
+// super-chunk's weight scales as load_scales left them, xb the slots'.  Blocks past K (the
+// padding of the last super-chunk) hold zero codes and zero scales on both
+// sides: their term is fma(0, +0, acc), which returns acc unchanged (acc
+// starts at +0 and no term can make it -0), so they need no test.
+template <int C, int RG, int CT>
+__device__ inline void mfma_chunk(const Chunk<RG, CT>& ch, const uint32_t ws[RG],
+                                  const SlotScales<CT>& xb, float acc[RG][CT][4]) {
+    uint32_t wd[RG][4];  // row 4*tq + r: block 2c's scale in the low half, 2c+1's in the high
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+        wd[rg][0] = chunk_scale<C, 0>(ws[rg]);
+        wd[rg][1] = chunk_scale<C, 1>(ws[rg]);
+        wd[rg][2] = chunk_scale<C, 2>(ws[rg]);
+        wd[rg][3] = chunk_scale<C, 3>(ws[rg]);
+    }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-        const _Float16 dx0 = half_bits(ch.dx[ct], 0), dx1 = half_bits(ch.dx[ct], 1);
+        const uint32_t dx = xb.template get<C>(ct);
+        const _Float16 dx0 = half_bits(dx, 0), dx1 = half_bits(dx, 1);
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
             const v4i zero = {0, 0, 0, 0};
             const v4i S0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(ch.w[rg].x, ch.aq[ct].x, zero, 0, 0, 0);
             const v4i S1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(ch.w[rg].y, ch.aq[ct].y, zero, 0, 0, 0);
-            // wd[rg]: row 4*tq + r has its block-2c scale in half 2r, block 2c+1 in 2r+1
             float* a = acc[rg][ct];
-            a[0] = term_fma(S0[0], half_bits(ch.wd[rg].x, 0), dx0, a[0]);
-            a[1] = term_fma(S0[1], half_bits(ch.wd[rg].y, 0), dx0, a[1]);
-            a[2] = term_fma(S0[2], half_bits(ch.wd[rg].z, 0), dx0, a[2]);
-            a[3] = term_fma(S0[3], half_bits(ch.wd[rg].w, 0), dx0, a[3]);
-            a[0] = term_fma(S1[0], half_bits(ch.wd[rg].x, 1), dx1, a[0]);
-            a[1] = term_fma(S1[1], half_bits(ch.wd[rg].y, 1), dx1, a[1]);
-            a[2] = term_fma(S1[2], half_bits(ch.wd[rg].z, 1), dx1, a[2]);
-            a[3] = term_fma(S1[3], half_bits(ch.wd[rg].w, 1), dx1, a[3]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] = term_fma(S0[r], half_bits(wd[rg][r], 0), dx0, a[r]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] = term_fma(S1[r], half_bits(wd[rg][r], 1), dx1, a[r]);
         }
+    }
+}
+
+// f(integral_constant<int, J>) for J = 0 .. N-1, in order.
+template <int J, int N, typename F>
+__device__ inline void static_for(F&& f) {
+    if constexpr (J < N) {
+        f(std::integral_constant<int, J>{});
+        static_for<J + 1, N>(f);
     }
 }
 
@@ -407,7 +488,7 @@ mm_mfma_kernel(MmArgs a) {
     const int split = SPLIT ? bid % a.S : w / a.KW;
     int sc0, sc1;
     slice_range(a.NSC, a.S, a.KW, split, SPLIT ? w : w % a.KW, sc0, sc1);
-    const int c_lo = 4 * sc0, c_hi = 4 * sc1;  // this wave's chunks (>= 4)
+    const int c_lo = 4 * sc0;  // this wave's chunks: [c_lo, 4 * sc1), at least one super-chunk
 
     // weights: RG consecutive row groups; the last row block may start
     // earlier (gbase < g0) so that every load stays inside the buffer, and
@@ -417,9 +498,11 @@ mm_mfma_kernel(MmArgs a) {
     const int64_t gq = (int64_t)a.NSC * kScQBytes;              // bytes per row group
     const int64_t gd = (int64_t)a.NSC * 4 * (kChunkDBytes / 2);  // halves per row group
     const uint8_t* wrow = a.wq + gbase * gq + lane * 16;
-    const uint16_t* wdrow = a.wd + gbase * gd + tq * 8;
+    // this lane's scale dword of a super-chunk: row 4*tq + (j & 3) of chunk j >> 2
+    const int jl = lane & 15;
+    const uint16_t* wsrow = a.wd + gbase * gd + ((jl >> 2) * kRowsPerGroup + 4 * tq + (jl & 3)) * 2;
     const uint8_t* xa = a.xq + lane * 16;
-    const uint16_t* xdp = a.xd + (lane & 15) * 2;
+    const uint16_t* xsrow = a.xd + lane * 2;
     const int gskip = (int)(g0 - gbase);
 
     float acc[RG][CT][4];
@@ -436,33 +519,54 @@ mm_mfma_kernel(MmArgs a) {
     int my_slot = 0;
     if ((int)threadIdx.x < 16 * CT && (int)threadIdx.x < a.n_live) my_slot = a.bidx[threadIdx.x];
 
+    // The ring: chunk c sits in ring[c % D].  The scales of the next
+    // super-chunk are loaded just before the first chunk of it, so waiting for
+    // that chunk covers them too.
     Chunk<RG, CT> ring[D];
+    uint32_t ws_next[RG], xs_next[CT];
+    load_scales<RG>(ws_next, sc0, wsrow, gd);
     if (FUSED) {
         // weights first; the slots only once the producers have published them
 #pragma unroll
-        for (int i = 0; i < D; ++i) load_chunk_w<RG, CT, NTW>(ring[i], c_lo + i, wrow, wdrow, gq, gd);
+        for (int i = 0; i < D; ++i) load_chunk_w<RG, CT, NTW>(ring[i], c_lo + i, wrow, gq);
         wait_for_slots(a, bid);
+        load_slot_scales<CT>(xs_next, sc0, xsrow, a.xd_gs);
 #pragma unroll
-        for (int i = 0; i < D; ++i) load_chunk_a<RG, CT>(ring[i], c_lo + i, xa, xdp, a.xq_gs, a.xd_gs);
+        for (int i = 0; i < D; ++i) load_chunk_a<RG, CT>(ring[i], c_lo + i, xa, a.xq_gs);
     } else {
+        load_slot_scales<CT>(xs_next, sc0, xsrow, a.xd_gs);
 #pragma unroll
-        for (int i = 0; i < D; ++i)
-            load_chunk<RG, CT, NTW>(ring[i], c_lo + i, wrow, wdrow, gq, gd, xa, xdp, a.xq_gs, a.xd_gs);
+        for (int i = 0; i < D; ++i) load_chunk<RG, CT, NTW>(ring[i], c_lo + i, wrow, gq, xa, a.xq_gs);
     }
-    int c = c_lo;
-    for (; c + D < c_hi; c += D) {
+    int sc = sc0;
+    SlotScales<CT> xb;
+    for (; sc + 1 < sc1; ++sc) {
+        uint32_t ws[RG];
 #pragma unroll
-        for (int i = 0; i < D; ++i) {
-            mfma_chunk<RG, CT>(ring[i], acc);
-            load_chunk<RG, CT, NTW>(ring[i], c + D + i, wrow, wdrow, gq, gd, xa, xdp, a.xq_gs, a.xd_gs);
+        for (int rg = 0; rg < RG; ++rg) ws[rg] = ws_next[rg];
+        xb.prepare(xs_next);
+        static_for<0, 4>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            mfma_chunk<j, RG, CT>(ring[j % D], ws, xb, acc);
+            if constexpr ((j + D) % 4 == 0) {
+                load_scales<RG>(ws_next, sc + 1, wsrow, gd);
+                load_slot_scales<CT>(xs_next, sc + 1, xsrow, a.xd_gs);
+            }
+            load_chunk<RG, CT, NTW>(ring[j % D], 4 * sc + j + D, wrow, gq, xa, a.xq_gs);
             // keep each chunk's loads right after its dot: left alone, the
-            // scheduler sinks all D chunks' loads to the end of the turn,
+            // scheduler sinks all the chunks' loads to the end of the turn,
             // and every turn then waits a full memory latency
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     }
-#pragma unroll
-    for (int i = 0; i < D; ++i) mfma_chunk<RG, CT>(ring[i], acc);
+    // the last super-chunk: its chunks are in the ring or loaded here
+    xb.prepare(xs_next);
+    static_for<0, 4>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        mfma_chunk<j, RG, CT>(ring[j % D], ws_next, xb, acc);
+        if constexpr (j + D < 4)
+            load_chunk<RG, CT, NTW>(ring[j % D], 4 * sc + j + D, wrow, gq, xa, a.xq_gs);
+    });
 
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
@@ -698,19 +802,17 @@ Tiling choose_tiling(const Shape& s) {
     // Rules measured on MI355X over the model-shaped matrices (K 5120..18432,
     // N 5120..151936):
     //  * two row groups per wave (each activation load feeds 32 rows);
-    //  * 4 waves per row block while there are fewer than 512 row blocks
-    //    (up to ~8k rows), else 8: enough waves in the grid to keep ~5 MB of
-    //    weights in flight, few enough that a row block's waves finish
-    //    together;
+    //  * 4 waves per row block: at ~90 registers a CU holds five such
+    //    workgroups, so a 35k-row matrix (1088 row blocks) runs in one round
+    //    instead of leaving a partial second round of 8-wave workgroups;
     //  * long rows (K >= 8192) are cut into 4 splits of one wave each, which
     //    the workspace entry point runs as separate single-row-group
     //    workgroups (more of them than there are CUs); shorter rows are one
-    //    split of 4 or 8 wave slices inside one workgroup;
+    //    split of 4 wave slices inside one workgroup;
     //  * never more wave slices than super-chunks.
     Tiling t;
     t.rg = s.G >= 2 ? 2 : 1;
-    const int64_t n_rb = (s.G + t.rg - 1) / t.rg;
-    const int P = n_rb < 512 ? 4 : 8;
+    const int P = 4;
     if (s.NSC >= 32) {
         t.splits = P;
         t.kw = 1;
