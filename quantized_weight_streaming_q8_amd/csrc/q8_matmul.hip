@@ -63,10 +63,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxKs = 16;             // waves per workgroup at most
-#ifndef Q8_RING
-#define Q8_RING 4
-#endif
-constexpr int kRing = Q8_RING;         // chunks in flight per wave (MFMA engine)
 constexpr size_t kMaxLds = 64 * 1024;  // dynamic LDS per workgroup we allow
 
 __device__ inline uint4 ld16(const void* p) {
@@ -475,7 +471,7 @@ mm_mfma_kernel(MmArgs a) {
         bid -= a.P;
     }
     static_assert(D == 1 || D == 2 || D == 4, "the ring depth must divide a super-chunk");
-    static_assert(RG == 1 || RG == 2, "row groups per wave");
+    static_assert(RG == 1 || RG == 2 || RG == 4, "row groups per wave");
     extern __shared__ __align__(16) float red[];
     __shared__ int last_flag;
     static_assert(CT >= 1 && CT * 16 <= kMaxColumns, "column tiles");
@@ -802,39 +798,73 @@ Tiling choose_tiling(const Shape& s) {
     // Rules measured on MI355X over the model-shaped matrices (K 5120..18432,
     // N 5120..151936):
     //  * two row groups per wave (each activation load feeds 32 rows);
-    //  * 4 waves per row block: at ~90 registers a CU holds five such
-    //    workgroups, so a 35k-row matrix (1088 row blocks) runs in one round
-    //    instead of leaving a partial second round of 8-wave workgroups;
     //  * long rows (K >= 8192) are cut into 4 splits of one wave each, which
     //    the workspace entry point runs as separate single-row-group
-    //    workgroups (more of them than there are CUs); shorter rows are one
-    //    split of 4 wave slices inside one workgroup;
+    //    workgroups (more of them than there are CUs), 4 chunks in flight
+    //    per wave;
+    //  * shorter rows are one split.  Below 512 row blocks (16k rows) it is
+    //    4 wave slices per row block with 4 chunks in flight each.  From 512
+    //    row blocks on, the weight stream runs fastest with about 4.4 MB in
+    //    flight over the whole GPU (more outstanding requests lower the
+    //    rate HBM delivers): one chunk in flight per wave and about 2200
+    //    waves, e.g. gate+up 5120->34816 at 2 slices, a 152k-row head at 1;
     //  * never more wave slices than super-chunks.
     Tiling t;
     t.rg = s.G >= 2 ? 2 : 1;
-    const int P = 4;
+    t.ring = 4;
     if (s.NSC >= 32) {
-        t.splits = P;
+        t.splits = 4;
         t.kw = 1;
         t.rg_split = 1;
     } else {
         t.splits = 1;
-        t.kw = (int)std::min<int64_t>(P, s.NSC);
         t.rg_split = t.rg;
+        const int64_t n_rb = (s.G + t.rg - 1) / t.rg;
+        int64_t kw = 4;
+        if (n_rb >= 512) {
+            kw = std::max<int64_t>(1, std::min<int64_t>(4, (2200 + n_rb / 2) / n_rb));
+            t.ring = 1;
+        }
+        t.kw = (int)std::min<int64_t>(kw, s.NSC);
     }
     t.nt_weights = true;
 #ifdef Q8_TUNING
     // measurement builds only: override the tiling from the environment
-    if (const char* e = getenv("Q8_RG")) t.rg = t.rg_split = atoi(e) == 2 ? 2 : 1;
+    if (const char* e = getenv("Q8_RG")) t.rg = t.rg_split = atoi(e) == 4 ? 4 : atoi(e) == 2 ? 2 : 1;
     if (const char* e = getenv("Q8_S")) t.splits = std::max(1, atoi(e));
     if (const char* e = getenv("Q8_KW")) t.kw = std::max(1, atoi(e));
     if (const char* e = getenv("Q8_NTW")) t.nt_weights = atoi(e) != 0;
+    if (const char* e = getenv("Q8_D")) t.ring = atoi(e) == 1 ? 1 : 4;
 #endif
     return t;
 }
 
 // Row groups per wave actually launched (a matrix with fewer row groups than
 // asked for runs one per wave).
+// The one-tile (16-slot) kernels: row groups per wave, split or not, and
+// ring depth as the tiling asks.
+template <bool FUSED>
+hipError_t launch_ct1(const MmArgs& a, int rg, bool split, int ring, bool nt_weights,
+                      hipStream_t st) {
+#define Q8_CT1(R, D)                                                               \
+    if (rg == R && ring == D)                                                      \
+        return split ? launch_mfma<R, 1, D, true, true, FUSED>(a, st)              \
+                     : launch_mfma<R, 1, D, true, false, FUSED>(a, st);
+#ifdef Q8_TUNING
+    // measurement builds only: plain-cached weight loads, four row groups
+    if (!nt_weights && !FUSED && ring == 4) {
+        if (rg == 2) return split ? launch_mfma<2, 1, 4, false, true>(a, st)
+                                  : launch_mfma<2, 1, 4, false, false>(a, st);
+        return split ? launch_mfma<1, 1, 4, false, true>(a, st) : launch_mfma<1, 1, 4, false, false>(a, st);
+    }
+    Q8_CT1(4, 4) Q8_CT1(4, 1)
+#endif
+    (void)nt_weights;
+    Q8_CT1(2, 4) Q8_CT1(2, 1) Q8_CT1(1, 4) Q8_CT1(1, 1)
+#undef Q8_CT1
+    return hipErrorInvalidValue;
+}
+
 int launch_rg(const Shape& s, const Tiling& t, bool split) {
     const int rg = split ? t.rg_split : t.rg;
     return s.G >= rg ? rg : 1;
@@ -915,18 +945,7 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
         }
 #undef Q8_LAUNCH_CT
     }
-#ifdef Q8_TUNING
-    if (!t.nt_weights) {
-        if (rg == 2) return split ? launch_mfma<2, 1, kRing, false, true>(a, st)
-                                  : launch_mfma<2, 1, kRing, false, false>(a, st);
-        return split ? launch_mfma<1, 1, kRing, false, true>(a, st)
-                     : launch_mfma<1, 1, kRing, false, false>(a, st);
-    }
-#endif
-    if (rg == 2) return split ? launch_mfma<2, 1, kRing, true, true>(a, st)
-                              : launch_mfma<2, 1, kRing, true, false>(a, st);
-    return split ? launch_mfma<1, 1, kRing, true, true>(a, st)
-                 : launch_mfma<1, 1, kRing, true, false>(a, st);
+    return launch_ct1<false>(a, rg, split, t.ring, t.nt_weights, st);
 }
 
 hipError_t launch_matmul_fused(const uint8_t* Wq, const float* X, int n_rows,
@@ -966,10 +985,10 @@ hipError_t launch_matmul_fused(const uint8_t* Wq, const float* X, int n_rows,
         a.counters = reinterpret_cast<uint32_t*>(ws);
         a.part = reinterpret_cast<float*>(ws + align_up((int64_t)a.n_rb * 4, 256));
     }
-    if (rg == 2) return split ? launch_mfma<2, 1, kRing, true, true, true>(a, st)
-                              : launch_mfma<2, 1, kRing, true, false, true>(a, st);
-    return split ? launch_mfma<1, 1, kRing, true, true, true>(a, st)
-                 : launch_mfma<1, 1, kRing, true, false, true>(a, st);
+    // 4 chunks in flight whatever the tiling says: the weights a wave puts in
+    // flight before it waits for the slots are what hides that wait (the
+    // ring depth does not change the sums)
+    return launch_ct1<true>(a, rg, split, 4, true, st);
 }
 
 }  // namespace q8
