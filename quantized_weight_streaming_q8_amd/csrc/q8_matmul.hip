@@ -127,8 +127,10 @@ struct MmArgs {
     int n_rows;
     int P;                // producer workgroups, blockIdx.x < P
     int n_cons;           // consumer (matmul) workgroups
-    uint32_t* qflag;      // producers that have published their slots
-    uint32_t* qdone;      // consumers past the wait
+    uint32_t* qflag;      // producer groups that have published their slots
+    uint32_t* qdone;      // consumer groups past the wait
+    uint32_t* qflag_sub;  // kSubCounters producer counters, kSubStride apart
+    uint32_t* qdone_sub;  // kSubCounters consumer counters, kSubStride apart
     uint32_t* qready;     // kReadyCopies "slots published" flags, kReadyStride apart
 };
 
@@ -379,14 +381,15 @@ __device__ inline TileOut tile_out(const MmArgs& a, const int* tok_slot, int o,
 // Fused pre-quantisation.  The first P workgroups of a FUSED launch quantise
 // X into the slot buffer (the q8_0 rule of the separate pre-quantiser, same
 // bits), write it with device-coherent stores, wait for the stores to
-// complete and bump qflag; the last of them raises the "published" flags.
+// complete and arrive at the producer counter (two levels, see arrive_last);
+// the last of them raises the "published" flags.
 // The matmul workgroups put their first weight chunks in flight, then wait
 // for their flag before their first activation load.  Workgroups are dispatched in index order, so the producers are
 // resident or done before any matmul workgroup waits, and they wait on
 // nothing themselves.  The wait is bounded all the same (kMaxSpins polls):
 // were it ever to run out, the outputs would be wrong (and tests would say
 // so) but the kernel would still finish.  The last matmul workgroup past the
-// wait rearms both counters for the next call.
+// wait rearms all the counters for the next call.
 // ------------------------------------------------------------------------
 
 constexpr int kMaxSpins = 1 << 22;
@@ -395,6 +398,24 @@ constexpr int kMaxSpins = 1 << 22;
 // that the polls of a large grid do not all queue on one memory channel.
 constexpr int kReadyCopies = 15;
 constexpr int kReadyStride = 1024;  // uint32 elements (4 KB)
+// Arrivals are counted in two levels: member id of n bumps counter id % 8,
+// the last of each of those bumps the top counter.  Atomics on one address
+// queue one behind the other at the memory side, so 1000 workgroups on one
+// counter take microseconds; 8 counters in different lines share the load.
+constexpr int kSubCounters = 8;
+constexpr int kSubStride = 32;  // uint32 elements (128 bytes)
+
+// True for the last of the n arrivals (ids 0 .. n-1, each arriving once).
+__device__ inline bool arrive_last(uint32_t* top, uint32_t* sub, int id, int n) {
+    const int s = id % kSubCounters;
+    const int groups = n < kSubCounters ? n : kSubCounters;
+    const uint32_t in_group = (uint32_t)((n - s + kSubCounters - 1) / kSubCounters);
+    if (__hip_atomic_fetch_add(sub + s * kSubStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+        in_group - 1)
+        return false;
+    return __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (uint32_t)(groups - 1);
+}
 
 __device__ void produce_slots(const MmArgs& a, int pid) {
     const int nthreads = blockDim.x;
@@ -432,9 +453,7 @@ __device__ void produce_slots(const MmArgs& a, int pid) {
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
-    if (threadIdx.x == 0 &&
-        __hip_atomic_fetch_add(a.qflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-            (uint32_t)(a.P - 1)) {
+    if (threadIdx.x == 0 && arrive_last(a.qflag, a.qflag_sub, pid, a.P)) {
         // the last producer: every slot is published; raise all the flags
         for (int k = 0; k < kReadyCopies; ++k)
             __hip_atomic_store(a.qready + k * kReadyStride, 1u, __ATOMIC_RELAXED,
@@ -575,11 +594,14 @@ mm_mfma_kernel(MmArgs a) {
     __syncthreads();
     if (FUSED && threadIdx.x == 0) {
         // every wave of this workgroup is past the wait: the last workgroup
-        // to get here rearms both counters
-        if (__hip_atomic_fetch_add(a.qdone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-            (uint32_t)(a.n_cons - 1)) {
+        // to get here rearms all the counters
+        if (arrive_last(a.qdone, a.qdone_sub, bid, a.n_cons)) {
             __hip_atomic_store(a.qflag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(a.qdone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int k = 0; k < kSubCounters; ++k) {
+                __hip_atomic_store(a.qflag_sub + k * kSubStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(a.qdone_sub + k * kSubStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
             for (int k = 0; k < kReadyCopies; ++k)
                 __hip_atomic_store(a.qready + k * kReadyStride, 0u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
@@ -973,6 +995,8 @@ hipError_t launch_matmul_fused(const uint8_t* Wq, const float* X, int n_rows,
     a.n_rows = n_rows;
     a.qflag = static_cast<uint32_t*>(workspace);
     a.qdone = a.qflag + 32;            // its own 128-byte line
+    a.qdone_sub = a.qflag + 64;        // 8 lines
+    a.qflag_sub = a.qflag + 64 + kSubCounters * kSubStride;  // 8 more, all in page 0
     a.qready = a.qflag + kReadyStride;  // pages 1..kReadyCopies
     if (a.S * a.KW > a.NSC) return hipErrorInvalidValue;
     const bool split = t.splits > 1;
