@@ -17,8 +17,11 @@ step time, the same at every live batch 1..16 with t(16)/t(1) and the
 speedup n*t(1)/t(n) over n single-token calls ("Batched decode: co-decode N
 live sessions in one GPU pass", section "Measured", compares ms/step against
 n x single-token time the same way), the roofline of the dominant kernel
-(the gate+up matmul) from HIP events on its stream, and the CPU oracle's
-rate on the host cores.
+(the gate+up matmul) from HIP events on its stream, each matrix's launch
+time as mean, median and p90 over 11 graph replays, the step time's median
+and p90 over 11 windows, a plain read-only streaming kernel's rate over 2
+GiB (the measured read ceiling, beside the 8 TB/s vendor peak), and the CPU
+oracle's rate on the host cores.
 """
 
 from __future__ import annotations
@@ -41,6 +44,7 @@ import workloads as wl  # noqa: E402
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, vendor figure
 COLD_BYTES = 1 << 30    # rotate weight copies past 1 GiB
 DOMINANT = "gate_up"
+STEP_REPEATS = 11       # windows for the step time's median and p90
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -197,6 +201,37 @@ def time_graph_steps(layer: Layer, n_live: int, steps: int, warmup: int):
     return dt * 1e3 / steps, same
 
 
+def graph_replay_us(launch, launches: int, replays: int) -> list:
+    """Per-launch duration of each of `replays` replays of one HIP graph that
+    holds `launches` back-to-back launches (launch(c) for c in
+    range(launches)), each replay between its own pair of HIP events on the
+    launch stream."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in range(4):
+            launch(c)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in range(launches):
+            launch(c)
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3 / launches)
+    del g
+    return out
+
+
 def graph_avg_us(launch, launches: int, replays: int = 3) -> float:
     """Average duration of one launch: `launches` back-to-back launches
     (launch(c) for c in range(launches)) captured in one HIP graph, replayed
@@ -226,6 +261,19 @@ def graph_avg_us(launch, launches: int, replays: int = 3) -> float:
     return e0.elapsed_time(e1) * 1e3 / (launches * replays)
 
 
+def kernel_stats_us(layer: Layer, i: int, n_live: int, launches: int, replays: int = 11) -> dict:
+    """Matrix i's narrow matmul, as kernel_avg_us, over `replays` graph
+    replays: the mean launch duration and the median and p90 of the
+    per-replay means."""
+    q8, m = layer.q8, layer.mats[i]
+    bi = layer.batch_index(n_live)
+    r = graph_replay_us(lambda c: q8.q8_matmul_narrow_ws(
+        layer.packed[c % layer.copies][i], layer.Xq[i], bi, n_live, m.N, m.K,
+        layer.Y[i], layer.ws[i]), launches, replays)
+    return {"mean": float(np.mean(r)), "median": float(np.median(r)),
+            "p90": float(np.percentile(r, 90)), "replays": replays, "launches_each": launches}
+
+
 def kernel_avg_us(layer: Layer, i: int, n_live: int, launches: int) -> float:
     """Average duration of one launch of matrix i's narrow matmul (the
     workspace entry point the step uses), back to back over the rotated
@@ -250,6 +298,27 @@ def quantize_avg_us(layer: Layer, i: int, launches: int = 100) -> float:
     """Average duration of one pre-quantize launch (16 rows of matrix i's K)."""
     q8, m = layer.q8, layer.mats[i]
     return graph_avg_us(lambda c: q8.q8_quantize_acts(layer.X[i], 16, m.K, layer.Xq[i]), launches)
+
+
+def read_ceiling_gbs(q8, nbytes: int = 2 << 30, reps: int = 10) -> float:
+    """Rate of the library's plain read-only streaming kernel over a 2 GiB
+    buffer (every byte read once per pass): the measured HBM read ceiling."""
+    import torch
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        q8.q8_stream_read(buf, nbytes, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        q8.q8_stream_read(buf, nbytes, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del buf
+    torch.cuda.empty_cache()
+    return nbytes / (ms * 1e-3) / 1e9
 
 
 def copy_ceiling_gbs(nbytes: int = 1 << 30, reps: int = 20) -> float:
@@ -599,7 +668,8 @@ def main(argv=None) -> int:
     per_matrix = {}
     kern_us, fused_us = [], []
     for i, m in enumerate(mats):
-        us = kernel_avg_us(layer, i, args.n_live, launches)
+        st = kernel_stats_us(layer, i, args.n_live, launches)
+        us = st["mean"]
         fu = fused_avg_us(layer, i, args.n_live, launches)
         kern_us.append(us)
         fused_us.append(fu)
@@ -607,6 +677,8 @@ def main(argv=None) -> int:
         fb = b + quantize_bytes(m.K)
         per_matrix[m.name] = {
             "K": m.K, "N": m.N, "us": round(us, 2), "GBps": round(b / us / 1e3, 1),
+            "us_median": round(st["median"], 2), "us_p90": round(st["p90"], 2),
+            "replays": st["replays"], "launches_per_replay": st["launches_each"],
             "frac_peak": round(b / us / 1e3 / PEAK_HBM_GBS, 4),
             "quantize_us": round(quantize_avg_us(layer, i), 2),
             "fused_us": round(fu, 2), "fused_GBps": round(fb / fu / 1e3, 1),
@@ -660,6 +732,16 @@ def main(argv=None) -> int:
     if rope:
         print(f"# pos-vector RoPE on the QKV rows: {rope['us']} us", file=sys.stderr, flush=True)
     copy_gbs = copy_ceiling_gbs()
+    read_gbs = read_ceiling_gbs(layer.q8)
+    print(f"# read ceiling (plain streaming read of 2 GiB): {read_gbs:.0f} GB/s; "
+          f"gate+up at {roofline['achieved'] / read_gbs:.0%} of it", file=sys.stderr, flush=True)
+    # the spread of the step time: STEP_REPEATS more windows of as many eager
+    # steps as the timed run, each between two device synchronisations
+    layer.fused = args.fused
+    win = [time_steps(layer, args.n_live, args.steps, 2, False)[0] for _ in range(STEP_REPEATS)]
+    repeats = {"windows": STEP_REPEATS, "steps_each": args.steps,
+               "median_ms": round(float(np.median(win)), 5),
+               "p90_ms": round(float(np.percentile(win, 90)), 5), "timing": "eager launches"}
     cpu = cpu_baseline(args.workload, args.n_live, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
     line = {
@@ -703,6 +785,8 @@ def main(argv=None) -> int:
         "multi_columns": multi,
         "rope_after_qkv": rope,
         "copy_ceiling_GBps": round(copy_gbs, 1),
+        "read_ceiling_GBps": round(read_gbs, 1),
+        "step_repeats": repeats,
         "cpu_baseline": cpu,
     }
     text = json.dumps(line)

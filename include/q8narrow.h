@@ -251,6 +251,21 @@ q8_status q8_matmul_multi(const void* Wq, const void* Xq, int n_slots,
 q8_status q8_rope_multi(float* Y, int n_rows, int64_t row_stride, const int32_t* pos,
                         int n_heads, int head_dim, double base, hipStream_t stream);
 
+/* --------------------------------------------------------- measurement */
+
+/* A plain read-only streaming kernel: reads every 16-byte unit of buf once
+ * (non-temporal loads, a grid-stride loop of 2048 x 256 threads) and
+ * computes nothing else.  Its rate over a large buffer is the measured HBM
+ * read ceiling against which the matmul's achieved bandwidth is set (the
+ * measurement section of the hot-path scope asks for it beside the vendor
+ * peak).  Each thread XORs the words it reads and writes sink[thread %
+ * 1024] only if that XOR equals 0x9E3779B9, so the loads cannot be dropped
+ * and, for ordinary data, nothing is written.
+ *
+ * buf: device, 16-byte aligned, bytes a positive multiple of 16 (at most
+ * 2^40); sink: device uint32 [1024], caller-owned.  Stream-ordered. */
+q8_status q8_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* ---------------------------------------------------------------- misc */
 
 /* 1 if the current HIP device is gfx950, 0 if not or if none is usable. */

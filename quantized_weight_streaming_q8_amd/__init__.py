@@ -52,6 +52,7 @@ _SIGNATURES = {
     "q8_quantize_acts_n": ([_vp, _i32, _i64, _vp, _i32, _vp], _i32),
     "q8_matmul_multi": ([_vp, _vp, _i32, _vp, _i32, _i64, _i64, _vp, _vp], _i32),
     "q8_rope_multi": ([_vp, _i32, _i64, _vp, _i32, _i32, ctypes.c_double, _vp], _i32),
+    "q8_stream_read": ([_vp, ctypes.c_size_t, _vp, _vp], _i32),
     "q8_device_supported": ([], _i32),
     "q8_status_str": ([_i32], ctypes.c_char_p),
 }
@@ -208,6 +209,10 @@ def q8_rope_multi(Y, n_rows: int, row_stride: int, pos, n_heads: int, head_dim: 
                   base: float, stream=None) -> None:
     _check(_lib.q8_rope_multi(_ptr(Y), n_rows, row_stride, _ptr(pos), n_heads, head_dim,
                               float(base), _stream(stream)), "q8_rope_multi")
+
+
+def q8_stream_read(buf, nbytes: int, sink, stream=None) -> None:
+    _check(_lib.q8_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "q8_stream_read")
 
 
 def q8_device_supported() -> bool:

@@ -213,6 +213,14 @@ q8_status q8_rope_multi(float* Y, int n_rows, int64_t row_stride, const int32_t*
                                           stream));
 }
 
+q8_status q8_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+    if (buf == nullptr || sink == nullptr || bytes == 0 || bytes % 16 != 0 ||
+        bytes > (size_t(1) << 40) || !aligned(buf, 16) || !aligned(sink, 4))
+        return Q8_ERR_INVALID_ARG;
+    if (!current_device_ok()) return Q8_ERR_UNSUPPORTED;
+    return from_hip(q8::launch_stream_read(buf, (int64_t)bytes, sink, stream));
+}
+
 int q8_device_supported(void) { return current_device_ok(); }
 
 const char* q8_status_str(q8_status status) {

@@ -1,0 +1,41 @@
+// q8_measure.hip -- a plain read-only streaming kernel, the measured HBM
+// read ceiling that the matmul's achieved bandwidth is set against.
+//
+// Every 16-byte unit of the buffer is read once, with non-temporal loads, by
+// a grid-stride loop of 2048 x 256 threads (the launch shape that read
+// fastest on MI355X).  Each thread XORs its words; it writes its sink entry
+// only when that XOR equals kMagic, so the loads cannot be dropped and the
+// kernel writes (practically) nothing.
+
+#include "q8_internal.h"
+
+namespace q8 {
+namespace {
+
+constexpr int kReadThreads = 256;
+constexpr int kReadBlocks = 2048;
+constexpr uint32_t kMagic = 0x9E3779B9u;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(kReadThreads)
+stream_read_kernel(const u32x4* __restrict__ p, int64_t n16, uint32_t* __restrict__ sink) {
+    const int64_t tid = (int64_t)blockIdx.x * kReadThreads + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kReadThreads;
+    uint32_t x = 0;
+    for (int64_t i = tid; i < n16; i += stride) {
+        const u32x4 v = __builtin_nontemporal_load(p + i);
+        x ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (x == kMagic) sink[tid & (kStreamSinkWords - 1)] = x;
+}
+
+}  // namespace
+
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t st) {
+    hipLaunchKernelGGL(stream_read_kernel, dim3(kReadBlocks), dim3(kReadThreads), 0, st,
+                       static_cast<const u32x4*>(buf), bytes / 16, sink);
+    return hipGetLastError();
+}
+
+}  // namespace q8

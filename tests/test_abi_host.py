@@ -29,7 +29,7 @@ def test_header_declares_the_abi():
     names = header_functions()
     for core in ("q8_pack_weights", "q8_quantize_acts", "q8_matmul_narrow"):
         assert core in names
-    assert len(names) == 18, names
+    assert len(names) == 19, names
 
 
 def test_every_declared_symbol_is_exported(q8):
@@ -239,3 +239,15 @@ def test_rope_rejects_invalid_arguments(q8):
     assert call(6, 1.0) == bad and call(6, float("nan")) == bad and call(6, -5.0) == bad
     assert call(0, None) == bad and call(0, P + 2) == bad    # Y null, misaligned
     assert call(3, None) == bad and call(3, P + 1) == bad    # pos null, misaligned
+
+
+def test_stream_read_rejects_invalid_arguments(q8):
+    lib = q8.library()
+    bad = q8.Q8_ERR_INVALID_ARG
+    assert lib.q8_stream_read(None, 1024, P, None) == bad          # no buffer
+    assert lib.q8_stream_read(P, 1024, None, None) == bad          # no sink
+    assert lib.q8_stream_read(P, 0, P, None) == bad                # empty
+    assert lib.q8_stream_read(P, 1000, P, None) == bad             # not whole 16-byte units
+    assert lib.q8_stream_read(P + 8, 1024, P, None) == bad         # misaligned buffer
+    assert lib.q8_stream_read(P, 1024, P + 2, None) == bad         # misaligned sink
+    assert lib.q8_stream_read(P, (1 << 40) + 16, P, None) == bad   # too large
