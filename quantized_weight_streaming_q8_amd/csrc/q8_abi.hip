@@ -11,6 +11,7 @@
 
 #include "q8narrow.h"
 #include "q8_internal.h"
+#include "q8_measure.h"
 
 #include <atomic>
 #include <cstring>

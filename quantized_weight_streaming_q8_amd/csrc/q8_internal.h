@@ -166,11 +166,6 @@ struct Tiling {
 };
 Tiling choose_tiling(const Shape& s);
 
-// Plain read of `bytes` (a multiple of 16) at buf, 16-byte aligned; sink
-// holds kStreamSinkWords uint32 (see q8_measure.hip).
-constexpr int kStreamSinkWords = 1024;
-hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t st);
-
 // Pos-vector RoPE in place on rows of Y (see q8_rope.hip).  Arguments are
 // validated by the caller.
 hipError_t launch_rope_multi(float* Y, int n_rows, int64_t row_stride, const int32_t* pos,

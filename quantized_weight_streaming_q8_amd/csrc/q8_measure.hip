@@ -7,7 +7,7 @@
 // only when that XOR equals kMagic, so the loads cannot be dropped and the
 // kernel writes (practically) nothing.
 
-#include "q8_internal.h"
+#include "q8_measure.h"
 
 namespace q8 {
 namespace {
