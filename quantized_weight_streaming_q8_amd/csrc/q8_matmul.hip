@@ -30,11 +30,12 @@
 //     against all 16 activation slots at once.  A = weights (row = lane & 15),
 //     B = slots (slot = lane & 15), D[row][slot] -> lane holds slot lane & 15
 //     for rows 4*(lane >> 4) + r, so a lane needs one slot's activation
-//     scales and four consecutive rows' weight scales, each one small load
-//     per chunk.  The cost is the same for any n_live: the weight stream is
-//     what the kernel spends its time on.  Tokens take their slot's column
-//     when the outputs are stored.  A wave covers RG row groups, so each
-//     activation load feeds 16*RG rows.
+//     scales and four consecutive rows' weight scales.  Both come once per
+//     super-chunk, one dword per lane, and reach the lanes that need them
+//     through DPP row broadcasts and permlane swaps.  The cost is the same
+//     for any n_live: the weight stream is what the kernel spends its time
+//     on.  Tokens take their slot's column when the outputs are stored.  A
+//     wave covers RG row groups, so each activation load feeds 16*RG rows.
 //   * DOT4: one output row per lane, v_dot4 over the row's 32 bytes against
 //     the token's block (wave-uniform, so it comes through scalar loads).  Its
 //     VALU work grows with n_live.
@@ -81,11 +82,6 @@ typedef __attribute__((address_space(4))) const u32x4 cu32x4;
 
 __device__ inline _Float16 half_bits(uint32_t w, int hi) {
     return __builtin_bit_cast(_Float16, (uint16_t)(w >> (16 * hi)));
-}
-
-__device__ inline _Float16 half_at(const uint4& v, int i) {
-    const uint32_t w = (i >> 1) == 0 ? v.x : (i >> 1) == 1 ? v.y : (i >> 1) == 2 ? v.z : v.w;
-    return half_bits(w, i & 1);
 }
 
 __device__ inline int live_slot(const int32_t* __restrict__ bidx, int n_live, int t) {
