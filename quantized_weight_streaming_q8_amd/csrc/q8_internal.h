@@ -161,7 +161,7 @@ struct Tiling {
     int rg_split;     // the same when the splits run as separate workgroups
     int splits;       // K splits (level 2 of the summation tree)
     int kw;           // wave slices per split (level 1)
-    int ring;         // chunks in flight per wave (1 or 4); no effect on the sums
+    int ring;         // chunks in flight per wave (1, 2 or 4); no effect on the sums
     bool nt_weights;  // non-temporal loads for the weight stream
 };
 Tiling choose_tiling(const Shape& s);

@@ -820,13 +820,18 @@ Tiling choose_tiling(const Shape& s) {
     //    the workspace entry point runs as separate single-row-group
     //    workgroups (more of them than there are CUs), 4 chunks in flight
     //    per wave;
-    //  * shorter rows are one split.  Below 512 row blocks (16k rows) it is
-    //    4 wave slices per row block with 4 chunks in flight each.  From 512
-    //    row blocks on, the weight stream runs fastest with about 4.4 MB in
-    //    flight over the whole GPU (more outstanding requests lower the
-    //    rate HBM delivers): one chunk in flight per wave and about 2200
-    //    waves, e.g. gate+up 5120->34816 at 2 slices, a 152k-row head at 1;
+    //  * shorter rows are one split.  Below 1024 row groups (16k rows) it is
+    //    two row groups per wave and 4 wave slices per row block, 4 chunks
+    //    in flight each.  From 1024 row groups on, the weight stream runs
+    //    fastest with about kInFlightKB of weights in flight over the whole
+    //    GPU (more outstanding requests lower the rate HBM delivers): one
+    //    wave per row group, covering the whole row, with the ring depth
+    //    (4, 2 or 1 chunks) that comes closest, e.g. 7168->18432 at 4,
+    //    gate+up 5120->34816 at 2.  Past kInFlightKB row groups even depth 1
+    //    is too much: two row groups per wave then halve the waves (a
+    //    152k-row head);
     //  * never more wave slices than super-chunks.
+    constexpr int64_t kInFlightKB = 4400;
     Tiling t;
     t.rg = s.G >= 2 ? 2 : 1;
     t.ring = 4;
@@ -836,13 +841,17 @@ Tiling choose_tiling(const Shape& s) {
         t.rg_split = 1;
     } else {
         t.splits = 1;
-        t.rg_split = t.rg;
-        const int64_t n_rb = (s.G + t.rg - 1) / t.rg;
         int64_t kw = 4;
-        if (n_rb >= 512) {
-            kw = std::max<int64_t>(1, std::min<int64_t>(4, (2200 + n_rb / 2) / n_rb));
-            t.ring = 1;
+        if (s.G >= 1024) {
+            kw = 1;
+            if (s.G <= kInFlightKB) {
+                t.rg = 1;
+                t.ring = 3 * s.G <= kInFlightKB ? 4 : 3 * s.G <= 2 * kInFlightKB ? 2 : 1;
+            } else {
+                t.ring = 1;
+            }
         }
+        t.rg_split = t.rg;
         t.kw = (int)std::min<int64_t>(kw, s.NSC);
     }
     t.nt_weights = true;
@@ -852,7 +861,7 @@ Tiling choose_tiling(const Shape& s) {
     if (const char* e = getenv("Q8_S")) t.splits = std::max(1, atoi(e));
     if (const char* e = getenv("Q8_KW")) t.kw = std::max(1, atoi(e));
     if (const char* e = getenv("Q8_NTW")) t.nt_weights = atoi(e) != 0;
-    if (const char* e = getenv("Q8_D")) t.ring = atoi(e) == 1 ? 1 : 4;
+    if (const char* e = getenv("Q8_D")) t.ring = atoi(e) == 1 ? 1 : atoi(e) == 2 ? 2 : 4;
 #endif
     return t;
 }
@@ -878,7 +887,10 @@ hipError_t launch_ct1(const MmArgs& a, int rg, bool split, int ring, bool nt_wei
     Q8_CT1(4, 4) Q8_CT1(4, 1)
 #endif
     (void)nt_weights;
-    Q8_CT1(2, 4) Q8_CT1(2, 1) Q8_CT1(1, 4) Q8_CT1(1, 1)
+    Q8_CT1(2, 4) Q8_CT1(2, 1) Q8_CT1(1, 4) Q8_CT1(1, 2) Q8_CT1(1, 1)
+#ifdef Q8_TUNING
+    Q8_CT1(2, 2)
+#endif
 #undef Q8_CT1
     return hipErrorInvalidValue;
 }
