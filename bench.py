@@ -155,10 +155,22 @@ def time_steps(layer: Layer, n_live: int, steps: int, warmup: int, with_events: 
     return dt * 1e3 / steps, kern
 
 
-def capture_step_graphs(layer: Layer, n_live: int):
-    """One HIP graph per weight copy, each holding one whole step (the four
-    quantise + matmul pairs), captured through torch's graph API on the
-    stream the library launches on."""
+def steps_per_graph(copies: int, steps: int, most: int = 40) -> int:
+    """Steps one captured graph holds: the largest multiple of the weight
+    copies that divides `steps` (so exactly `steps` steps are replayed) and
+    is at most `most`; 1 if there is none."""
+    best = 1
+    for n in range(copies, most + 1, copies):
+        if steps % n == 0:
+            best = n
+    return best
+
+
+def capture_step_graph(layer: Layer, n_live: int, spg: int):
+    """One HIP graph holding `spg` whole steps (each the four quantise +
+    matmul pairs, the weight copies in rotation), captured through torch's
+    graph API on the stream the library launches on.  With several steps per
+    graph, the host's cost of launching a graph is spread over them."""
     import torch
     bi = layer.batch_index(n_live)
     side = torch.cuda.Stream()
@@ -168,37 +180,37 @@ def capture_step_graphs(layer: Layer, n_live: int):
             layer.step(c, bi, n_live)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    graphs = []
-    for c in range(layer.copies):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            layer.step(c, bi, n_live)
-        graphs.append(g)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(spg):
+            layer.step(k % layer.copies, bi, n_live)
     torch.cuda.synchronize()
-    return graphs, bi
+    return g, bi
 
 
 def time_graph_steps(layer: Layer, n_live: int, steps: int, warmup: int):
-    """Step time with each step replayed from a captured graph.  Returns
-    (ms per step, True if every output of the last replay is bit-identical
-    to an eager step on the same inputs)."""
+    """Step time with the steps replayed from captured graphs of several
+    steps each (exactly `steps` steps in all).  Returns (ms per step, True if
+    every output of the last replay is bit-identical to an eager step on the
+    same inputs, steps per graph)."""
     import torch
-    graphs, bi = capture_step_graphs(layer, n_live)
-    for s in range(warmup):
-        graphs[s % layer.copies].replay()
+    spg = steps_per_graph(layer.copies, steps)
+    g, bi = capture_step_graph(layer, n_live, spg)
+    for _ in range(max(1, warmup // spg)):
+        g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(steps):
-        graphs[s % layer.copies].replay()
+    for _ in range(steps // spg):
+        g.replay()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    last = (steps - 1) % layer.copies
+    last = (spg - 1) % layer.copies
     got = [y.clone() for y in layer.Y]
     layer.step(last, bi, n_live)
     torch.cuda.synchronize()
     same = all(torch.equal(a.view(torch.int32), b.view(torch.int32)) for a, b in zip(got, layer.Y))
-    del graphs
-    return dt * 1e3 / steps, same
+    del g
+    return dt * 1e3 / steps, same, spg
 
 
 def graph_replay_us(launch, launches: int, replays: int) -> list:
@@ -642,11 +654,14 @@ def main(argv=None) -> int:
         ms_e, _ = time_steps(layer, n_live, steps, warmup, with_events=False)
         ms_g = None
         if args.graph:
-            ms_g, ok = time_graph_steps(layer, n_live, steps, warmup)
+            ms_g, ok, spg = time_graph_steps(layer, n_live, steps, warmup)
+            graph_steps[0] = spg
             if not ok:
                 ms_g = None
         best = ms_e if ms_g is None or ms_e <= ms_g else ms_g
         return best, ms_e, ms_g
+
+    graph_steps = [None]
 
     # the step the library's fused entry point runs (one launch per matrix),
     # and the same step as separate pre-quantise and matmul launches
@@ -753,8 +768,8 @@ def main(argv=None) -> int:
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "ms_per_step_eager": round(ms_eager, 5),
-        "timing": ("hip graph replay per step (checked bit-identical to eager)" if ms is not ms_eager
-                   else "eager launches on one stream") + "; the faster of the two",
+        "timing": (f"hip graph replay, {graph_steps[0]} steps per graph (checked bit-identical to eager)"
+                   if ms is not ms_eager else "eager launches on one stream") + "; the faster of the two",
         "ms_per_step_graph": round(ms_graph, 5) if ms_graph is not None else None,
         "step_launches": "fused pre-quantise + matmul, one launch per matrix" if args.fused
         else "separate pre-quantise and matmul launches",

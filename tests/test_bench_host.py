@@ -47,3 +47,14 @@ def test_step_bytes_of_the_qwen3_layer():
 
 def test_more_than_one_gpu_is_refused():
     assert bench.main(["--gpus", "2"]) == 2
+
+
+def test_steps_per_graph_divides_the_timed_steps():
+    import bench
+    assert bench.steps_per_graph(4, 400) == 40
+    assert bench.steps_per_graph(4, 100) == 20
+    assert bench.steps_per_graph(4, 50) == 1      # no multiple of 4 divides 50
+    assert bench.steps_per_graph(3, 9) == 9
+    for copies, steps in ((4, 400), (4, 100), (2, 30), (5, 7)):
+        n = bench.steps_per_graph(copies, steps)
+        assert steps % n == 0 and (n == 1 or n % copies == 0)
