@@ -652,23 +652,20 @@ def main(argv=None) -> int:
         """(ms per step, eager ms, graph ms or None): the faster of eager
         launches and graph replay (the replay checked against eager)."""
         ms_e, _ = time_steps(layer, n_live, steps, warmup, with_events=False)
-        ms_g = None
+        ms_g, spg = None, None
         if args.graph:
             ms_g, ok, spg = time_graph_steps(layer, n_live, steps, warmup)
-            graph_steps[0] = spg
             if not ok:
                 ms_g = None
         best = ms_e if ms_g is None or ms_e <= ms_g else ms_g
-        return best, ms_e, ms_g
-
-    graph_steps = [None]
+        return best, ms_e, ms_g, spg
 
     # the step the library's fused entry point runs (one launch per matrix),
     # and the same step as separate pre-quantise and matmul launches
     layer.fused = args.fused
-    ms, ms_eager, ms_graph = step_time(args.n_live, args.steps, args.warmup)
+    ms, ms_eager, ms_graph, graph_spg = step_time(args.n_live, args.steps, args.warmup)
     layer.fused = not args.fused
-    ms_other, _, _ = step_time(args.n_live, args.steps, args.warmup)
+    ms_other = step_time(args.n_live, args.steps, args.warmup)[0]
     layer.fused = args.fused
     nbytes = step_bytes(mats, args.n_live)
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -723,7 +720,7 @@ def main(argv=None) -> int:
     sweep = {}
     if args.sweep_steps > 0:
         for n in range(1, 17):
-            ms_n, ms_e, _ = step_time(n, args.sweep_steps, min(args.warmup, 20))
+            ms_n, ms_e, _, _ = step_time(n, args.sweep_steps, min(args.warmup, 20))
             kn = [kernel_avg_us(layer, i, n, max(16, 2 * layer.copies)) for i in range(len(mats))]
             sweep[n] = {"ms_per_step": round(ms_n, 4), "ms_per_step_eager": round(ms_e, 4),
                         "GBps": round(step_bytes(mats, n) / (ms_n * 1e-3) / 1e9, 1),
@@ -768,7 +765,7 @@ def main(argv=None) -> int:
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "ms_per_step_eager": round(ms_eager, 5),
-        "timing": (f"hip graph replay, {graph_steps[0]} steps per graph (checked bit-identical to eager)"
+        "timing": (f"hip graph replay, {graph_spg} steps per graph (checked bit-identical to eager)"
                    if ms is not ms_eager else "eager launches on one stream") + "; the faster of the two",
         "ms_per_step_graph": round(ms_graph, 5) if ms_graph is not None else None,
         "step_launches": "fused pre-quantise + matmul, one launch per matrix" if args.fused
