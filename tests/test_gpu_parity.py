@@ -151,6 +151,38 @@ def test_matmul_ragged_shapes(N, K):
         assert np.array_equal(Ym.view(np.uint32), Yw.view(np.uint32)), (N, K, bi)
 
 
+# Large ragged shapes that reach each tiling the default rule picks for 1024+
+# row groups: one row group per wave with 4 (G <= 1466), 2 (G <= 2933) or 1
+# (G <= 4400) chunks in flight, and two row groups per wave past 4400; N is
+# not a multiple of 16 and K leaves the last super-chunk partly empty.
+@pytest.mark.parametrize("N,K", [(16391, 4128), (32005, 800), (48003, 1056), (72009, 800)])
+def test_matmul_large_ragged_shapes(N, K):
+    rng = np.random.default_rng(N - K)
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    X = _ragged_x(K, seed=K + 2)
+    Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
+    import quantized_weight_streaming_q8_amd as q8
+    ws = q8.zeroed_workspace(N, K)
+    rows = sample_rows(N, 96, seed=N)
+    for bi in (rng.permutation(16), np.array([5, 5, 0, 12])):
+        bi = bi.astype(np.int32)
+        Yo, Ao = _oracle_y(W, X, bi, rows)
+        Ym = gpu_matmul(Wq, Xq, bi, N, K, MFMA)
+        ok, worst = within_tau(Ym[:, rows], Yo, Ao)
+        assert ok, (N, K, bi, worst)
+        Yw = gpu_matmul_ws(Wq, Xq, bi, N, K, ws)
+        assert np.array_equal(Ym.view(np.uint32), Yw.view(np.uint32)), (N, K, bi)
+        Yd = gpu_matmul(Wq, Xq, bi, N, K, DOT4)
+        assert np.array_equal(Ym.view(np.uint32), Yd.view(np.uint32)), (N, K, bi)
+    # every column is its slot's column of the full 16-slot call
+    full = gpu_matmul(Wq, Xq, np.arange(16, dtype=np.int32), N, K, MFMA)
+    bi = np.array([7, 3, 3, 14], dtype=np.int32)
+    Yb = gpu_matmul(Wq, Xq, bi, N, K, MFMA)
+    assert np.array_equal(Yb.view(np.uint32), full[bi].view(np.uint32))
+    del Wq
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("n_live", [1, 2, 4])
 def test_single_768(n_live):
     w = wl.WORKLOADS["single"]
