@@ -290,6 +290,15 @@ struct SlotScales {
     }
 };
 
+// f(integral_constant<int, J>) for J = 0 .. N-1, in order.
+template <int J, int N, typename F>
+__device__ inline void static_for(F&& f) {
+    if constexpr (J < N) {
+        f(std::integral_constant<int, J>{});
+        static_for<J + 1, N>(f);
+    }
+}
+
 // Dot chunk C of a super-chunk and accumulate: acc[rg][ct][r] is row
 // 4*tq + r of row group rg for slot 16*ct + (lane & 15); ws[rg] holds the
 // super-chunk's weight scales as load_scales left them, xb the slots'.  Blocks past K (the
@@ -307,31 +316,33 @@ __device__ inline void mfma_chunk(const Chunk<RG, CT>& ch, const uint32_t ws[RG]
         wd[rg][2] = chunk_scale<C, 2>(ws[rg]);
         wd[rg][3] = chunk_scale<C, 3>(ws[rg]);
     }
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
+    // The (tile, row group) pairs in order, their two MFMAs issued one pair
+    // ahead of the scale arithmetic that consumes them, so that a result is
+    // never waited for right after its MFMA.  Each accumulator still takes
+    // its block-2c term, then its block-2c+1 term.
+    constexpr int P = CT * RG;
+    const v4i zero = {0, 0, 0, 0};
+    v4i S[2][2];
+    S[0][0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(ch.w[0].x, ch.aq[0].x, zero, 0, 0, 0);
+    S[0][1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(ch.w[0].y, ch.aq[0].y, zero, 0, 0, 0);
+    static_for<0, P>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        constexpr int ct = p / RG, rg = p % RG;
+        if constexpr (p + 1 < P) {
+            constexpr int ct1 = (p + 1) / RG, rg1 = (p + 1) % RG;
+            S[(p + 1) & 1][0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(ch.w[rg1].x, ch.aq[ct1].x, zero, 0, 0, 0);
+            S[(p + 1) & 1][1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(ch.w[rg1].y, ch.aq[ct1].y, zero, 0, 0, 0);
+        }
         const uint32_t dx = xb.template get<C>(ct);
         const _Float16 dx0 = half_bits(dx, 0), dx1 = half_bits(dx, 1);
+        const v4i& S0 = S[p & 1][0];
+        const v4i& S1 = S[p & 1][1];
+        float* a = acc[rg][ct];
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-            const v4i zero = {0, 0, 0, 0};
-            const v4i S0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(ch.w[rg].x, ch.aq[ct].x, zero, 0, 0, 0);
-            const v4i S1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(ch.w[rg].y, ch.aq[ct].y, zero, 0, 0, 0);
-            float* a = acc[rg][ct];
+        for (int r = 0; r < 4; ++r) a[r] = term_fma(S0[r], half_bits(wd[rg][r], 0), dx0, a[r]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) a[r] = term_fma(S0[r], half_bits(wd[rg][r], 0), dx0, a[r]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) a[r] = term_fma(S1[r], half_bits(wd[rg][r], 1), dx1, a[r]);
-        }
-    }
-}
-
-// f(integral_constant<int, J>) for J = 0 .. N-1, in order.
-template <int J, int N, typename F>
-__device__ inline void static_for(F&& f) {
-    if constexpr (J < N) {
-        f(std::integral_constant<int, J>{});
-        static_for<J + 1, N>(f);
-    }
+        for (int r = 0; r < 4; ++r) a[r] = term_fma(S1[r], half_bits(wd[rg][r], 1), dx1, a[r]);
+    });
 }
 
 // Loads and stores that are coherent across the whole device (all XCDs)
