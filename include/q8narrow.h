@@ -156,9 +156,14 @@ size_t q8_matmul_workspace_bytes(int64_t N, int64_t K);
  * partial sums, and the last to arrive adds them in split order.  The result
  * is bit-identical to q8_matmul_narrow on the same arguments.
  *
- * The workspace must be zero-filled before its first use; every completed
- * call leaves it ready for the next one.  A workspace must not be shared by
- * calls that can run at the same time (calls on one stream are fine).
+ * The workspace must be zero-filled before its first use.  Every completed
+ * call leaves it ready for the next one, on a matrix of the same shape or of
+ * any other (as long as the workspace is large enough for it): the arrival
+ * counters are back at zero, and the partial sums left behind sit where no
+ * shape keeps a counter.  A workspace must not be shared by calls that can
+ * run at the same time (calls on one stream are fine), nor between this
+ * entry point and q8_matmul_narrow_fused, whose workspace is laid out
+ * differently, without being zero-filled again in between.
  * workspace may be NULL when q8_matmul_workspace_bytes(N, K) is 0.  A
  * workspace that is missing, misaligned or too small is an invalid
  * argument. */
@@ -188,8 +193,10 @@ size_t q8_matmul_fused_workspace_bytes(int64_t N, int64_t K);
  *
  * workspace: device memory, 256-byte aligned, at least
  * q8_matmul_fused_workspace_bytes(N, K) bytes, zero-filled before its first
- * use; every completed call leaves it zero again.  It must not be shared by
- * calls that can run at the same time.  1 <= n_rows, n_live <= Q8_MAX_SLOTS;
+ * use.  Every completed call leaves its counters and flags at zero again (as
+ * with q8_matmul_narrow_ws, partial sums left behind are never taken for
+ * counters), so it may serve matrices of any shape in turn.  It must not be
+ * shared by calls that can run at the same time.  1 <= n_rows, n_live <= Q8_MAX_SLOTS;
  * X fp32 [n_rows][K], 16-byte aligned. */
 q8_status q8_matmul_narrow_fused(const void* Wq, const float* X, int n_rows, void* Xq,
                                  const int32_t* batch_index, int n_live, int64_t N,

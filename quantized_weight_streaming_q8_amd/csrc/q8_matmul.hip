@@ -20,7 +20,8 @@
 // waves (levels 1 and 2 through LDS).  The workspace entry point runs the S
 // splits of a row block as S workgroups: each evaluates level 1 and writes
 // its partial to the workspace; the last of them to arrive (a counter per
-// row block) evaluates level 2 and writes Y.  Both give the same bits, and
+// row block) evaluates level 2, writes Y and rearms the counter.  Both give
+// the same bits, and
 // so does the DOT4 engine below, so a token's output never depends on
 // n_live, on the other tokens or on the entry point.
 //
@@ -108,8 +109,7 @@ struct MmArgs {
     const uint16_t* xd;   // activation slots: scale region
     const int32_t* bidx;  // batch_index
     float* Y;
-    uint32_t* counters;   // workspace: one arrival counter per row block
-    float* part;          // workspace: split partials [S][row block][tile]
+    uint8_t* recs;        // workspace: one record per row block (see split_record)
     int64_t N;
     int64_t G;
     int KB, NSC, n_live;
@@ -152,6 +152,28 @@ __device__ inline float tree_sum(const float* red, int E, int e, int S, int KW) 
     float y = split_sum(red, E, e, 0, KW);
     for (int s = 1; s < S; ++s) y += split_sum(red, E, e, s, KW);
     return y;
+}
+
+// The workspace of a split execution is one record per row block: the
+// block's arrival counter alone in a 256-byte line, then the S split
+// partials of its E-element tile.  Every split shape runs S = 4 splits of a
+// one-row-group, one-column-tile tile (E = 256), so the records of every
+// shape have the same stride: a counter of one shape always sits where
+// every other shape keeps a counter, never where partials were.  A
+// workspace whose counters every call rearms may therefore serve matrices
+// of any shape in turn.
+constexpr int64_t kRecordHead = 256;
+
+__host__ __device__ inline int64_t record_bytes(int S, int E) {
+    return kRecordHead + (int64_t)S * E * (int64_t)sizeof(float);
+}
+
+__device__ inline uint32_t* record_counter(uint8_t* recs, int rb, int S, int E) {
+    return reinterpret_cast<uint32_t*>(recs + rb * record_bytes(S, E));
+}
+
+__device__ inline float* record_part(uint8_t* recs, int rb, int S, int E, int split) {
+    return reinterpret_cast<float*>(recs + rb * record_bytes(S, E) + kRecordHead) + split * E;
 }
 
 // ------------------------------------------------------------------------
@@ -629,7 +651,7 @@ mm_mfma_kernel(MmArgs a) {
     // The partials are written with device-coherent stores and the wait below
     // makes them complete before the counter moves, so no cache has to be
     // flushed; the last split reads them back with device-coherent loads.
-    float* mine = a.part + ((int64_t)split * a.n_rb + rb) * E;
+    float* mine = record_part(a.recs, rb, a.S, E, split);
     for (int e = threadIdx.x; e < E; e += nthreads) coherent_store(mine + e, split_sum(red, E, e, 0, a.KW));
     // every thread waits for its own stores to complete before the barrier,
     // so the counter can only move once the whole partial is in place
@@ -638,7 +660,7 @@ mm_mfma_kernel(MmArgs a) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
     if (threadIdx.x == 0)
-        last_flag = __hip_atomic_fetch_add(a.counters + rb, 1u, __ATOMIC_RELAXED,
+        last_flag = __hip_atomic_fetch_add(record_counter(a.recs, rb, a.S, E), 1u, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(a.S - 1);
     __syncthreads();
     if (!last_flag) return;
@@ -659,7 +681,7 @@ mm_mfma_kernel(MmArgs a) {
 #pragma unroll
                 for (int s = 0; s < kCombineSplits; ++s)
                     p[k][s] = (to[k].store && s < a.S)
-                                  ? coherent_load(a.part + ((int64_t)s * a.n_rb + rb) * E + to[k].e)
+                                  ? coherent_load(record_part(a.recs, rb, a.S, E, s) + to[k].e)
                                   : 0.0f;
             }
 #pragma unroll
@@ -676,13 +698,15 @@ mm_mfma_kernel(MmArgs a) {
         for (int o = threadIdx.x; o < E; o += nthreads) {
             const TileOut to = tile_out<RG, CT>(a, tok_slot, o, gbase, gskip);
             if (!to.store) continue;
-            float y = coherent_load(a.part + (int64_t)rb * E + to.e);
+            float y = coherent_load(record_part(a.recs, rb, a.S, E, 0) + to.e);
             for (int s = 1; s < a.S; ++s)
-                y += coherent_load(a.part + ((int64_t)s * a.n_rb + rb) * E + to.e);
+                y += coherent_load(record_part(a.recs, rb, a.S, E, s) + to.e);
             a.Y[(int64_t)to.t * a.N + to.n] = to.bad ? __builtin_nanf("") : y;
         }
     }
-    if (threadIdx.x == 0) __hip_atomic_store(a.counters + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+        __hip_atomic_store(record_counter(a.recs, rb, a.S, E), 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 int mfma_waves(const MmArgs& a, bool split) { return split ? a.KW : a.S * a.KW; }
@@ -915,8 +939,7 @@ size_t workspace_bytes(const Shape& s, const Tiling& t) {
     if (t.splits <= 1) return 0;
     const int rg = launch_rg(s, t, true);
     const int64_t n_rb = (s.G + rg - 1) / rg;
-    const int64_t counters = align_up(n_rb * 4, 256);
-    return (size_t)(counters + (int64_t)t.splits * n_rb * rg * 256 * 4);
+    return (size_t)(n_rb * record_bytes(t.splits, rg * 256));
 }
 
 hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
@@ -947,13 +970,7 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
     if (split && a.CT != 1) return hipErrorInvalidValue;
     const int rg = launch_rg(s, t, split);
     a.n_rb = (int)((s.G + rg - 1) / rg);
-    a.counters = nullptr;
-    a.part = nullptr;
-    if (split) {
-        a.counters = static_cast<uint32_t*>(workspace);
-        a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                          align_up((int64_t)a.n_rb * 4, 256));
-    }
+    a.recs = split ? static_cast<uint8_t*>(workspace) : nullptr;
     // more than one column tile: a shallower ring keeps the chunk operands
     // (which grow with the tiles) in registers
     if (a.CT > 1) {
@@ -1021,13 +1038,7 @@ hipError_t launch_matmul_fused(const uint8_t* Wq, const float* X, int n_rows,
     const bool split = t.splits > 1;
     const int rg = launch_rg(s, t, split);
     a.n_rb = (int)((s.G + rg - 1) / rg);
-    a.counters = nullptr;
-    a.part = nullptr;
-    if (split) {
-        uint8_t* ws = static_cast<uint8_t*>(workspace) + kFusedFlagBytes;
-        a.counters = reinterpret_cast<uint32_t*>(ws);
-        a.part = reinterpret_cast<float*>(ws + align_up((int64_t)a.n_rb * 4, 256));
-    }
+    a.recs = split ? static_cast<uint8_t*>(workspace) + kFusedFlagBytes : nullptr;
     // 4 chunks in flight whatever the tiling says: the weights a wave puts in
     // flight before it waits for the slots are what hides that wait (the
     // ring depth does not change the sums)

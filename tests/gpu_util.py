@@ -106,3 +106,15 @@ def sample_rows(N: int, n: int, seed: int) -> np.ndarray:
     rest = rng.choice(N, size=min(N, n), replace=False)
     rows = np.unique(np.clip(np.concatenate([fixed, rest]), 0, N - 1))
     return rows.astype(np.int64)
+
+
+def split_counters_clear(ws, N: int, K: int, offset: int = 0) -> bool:
+    """True if every row block's arrival counter in a split workspace (from
+    byte `offset` on) is zero.  The workspace is one equal-sized record per
+    row block of 16 rows, each starting with its counter's 256-byte line."""
+    nbytes = q8().q8_matmul_workspace_bytes(N, K)
+    n_rb = -(-N // 16)
+    rec = nbytes // n_rb
+    assert rec * n_rb == nbytes and rec > 256
+    heads = ws[offset:offset + nbytes].view(n_rb, rec)[:, :256]
+    return not heads.any()

@@ -140,11 +140,13 @@ def test_other_entry_points_reject_invalid_arguments(q8):
 
 def test_workspace_sizes(q8):
     # long rows (K >= 8192) are split across workgroups and need a workspace:
-    # a counter per row group (256-byte aligned) and 4 partial tiles of
-    # 16 x 16 fp32 per row group; shorter rows are not split
-    G = 5120 // 16
-    assert q8.q8_matmul_workspace_bytes(5120, 17408) == -(-G * 4 // 256) * 256 + 4 * G * 1024
-    assert q8.q8_matmul_workspace_bytes(7168, 18432) > 0
+    # one record per row group, its counter's 256-byte line then 4 partial
+    # tiles of 16 x 16 fp32, the same record size for every split shape;
+    # shorter rows are not split
+    rec = 256 + 4 * 1024
+    assert q8.q8_matmul_workspace_bytes(5120, 17408) == (5120 // 16) * rec
+    assert q8.q8_matmul_workspace_bytes(7168, 18432) == (7168 // 16) * rec
+    assert q8.q8_matmul_workspace_bytes(1000, 8224) == 63 * rec
     assert q8.q8_matmul_workspace_bytes(5120, 5120) == 0
     assert q8.q8_matmul_workspace_bytes(151936, 5120) == 0
     assert q8.q8_matmul_workspace_bytes(0, 5120) == 0

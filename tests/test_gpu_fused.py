@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_util import gpu_pack, sample_rows, to_dev, within_tau
+from gpu_util import gpu_pack, sample_rows, split_counters_clear, to_dev, within_tau
 
 pytestmark = pytest.mark.gpu
 
@@ -40,13 +40,14 @@ def _x(n, K, seed):
 
 
 def _counters_clear(ws, N, K):
-    """The fused counters and flags and, for split shapes, the split counters (one per
-    row group) are back to zero; the partial sums after them may hold
-    anything."""
-    n = 65536
+    """The fused counters and flags (the first 64 KB) and, for split shapes,
+    every row block's split counter are back to zero; the partial sums may
+    hold anything."""
+    if ws[:65536].any():
+        return False
     if _q8().q8_matmul_workspace_bytes(N, K) > 0:
-        n += -(-(-(-N // 16)) * 4 // 256) * 256
-    return not ws[:n].any()
+        return split_counters_clear(ws, N, K, offset=65536)
+    return True
 
 
 def _separate(Wq, X, Xq, bi, N, K):

@@ -14,7 +14,7 @@ import oracle
 import workloads as wl
 from gpu_util import (gpu_matmul, gpu_matmul_ws, gpu_pack, gpu_pack_q,
                       gpu_quantize_acts, gpu_unpack, sample_rows, slots_host,
-                      to_dev, within_tau, write_slots)
+                      split_counters_clear, to_dev, within_tau, write_slots)
 
 pytestmark = pytest.mark.gpu
 
@@ -275,8 +275,8 @@ def test_bad_batch_index_gives_nan_row():
 
 def test_workspace_is_rearmed_by_every_call():
     """A workspace used by many calls in a row (and by calls with different
-    live batches) keeps giving the plain entry point's bits, and is all zero
-    again after each call."""
+    live batches) keeps giving the plain entry point's bits, and has every
+    row block's arrival counter back at zero after each call."""
     import quantized_weight_streaming_q8_amd as q8
     rng = np.random.default_rng(37)
     N, K = 5120, 17408  # long rows: the workspace entry point splits K across workgroups
@@ -285,14 +285,39 @@ def test_workspace_is_rearmed_by_every_call():
     X = rng.standard_normal((16, K), dtype=np.float32)
     Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
     ws = q8.zeroed_workspace(N, K)
-    nbytes_counters = -(-(-(-N // 16)) * 4 // 256) * 256
     for rep in range(3):
         for n in (16, 1, 5):
             bi = rng.permutation(16)[:n].astype(np.int32)
             Yp = gpu_matmul(Wq, Xq, bi, N, K)
             Yw = gpu_matmul_ws(Wq, Xq, bi, N, K, ws)
             assert np.array_equal(Yp.view(np.uint32), Yw.view(np.uint32)), (rep, n)
-            assert not ws[:nbytes_counters].any()
+            assert split_counters_clear(ws, N, K), (rep, n)
+
+
+def test_one_workspace_serves_every_shape():
+    """One workspace shared by split matrices of different row-block counts,
+    in turns: each call gives the plain entry point's bits.  The partial sums
+    a call leaves behind must never sit where another shape keeps a counter
+    (with the counters of all row blocks first and the partials after them,
+    a shape with more row blocks would find them there)."""
+    import quantized_weight_streaming_q8_amd as q8
+    rng = np.random.default_rng(41)
+    shapes = [(3000, 8448), (600, 9024), (2000, 8192)]  # 188, 38, 125 row groups
+    mats = []
+    for N, K in shapes:
+        assert q8.q8_matmul_workspace_bytes(N, K) > 0, (N, K)
+        W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+        X = rng.standard_normal((16, K), dtype=np.float32)
+        mats.append((N, K, gpu_pack(W), gpu_quantize_acts(X)))
+    nbytes = max(q8.q8_matmul_workspace_bytes(N, K) for N, K in shapes)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for rep, i in enumerate((0, 1, 2, 0, 1, 2, 1)):
+        N, K, Wq, Xq = mats[i]
+        bi = rng.permutation(16)[: 1 + rep * 2].astype(np.int32)
+        Yp = gpu_matmul(Wq, Xq, bi, N, K)
+        Yw = gpu_matmul_ws(Wq, Xq, bi, N, K, ws)
+        assert np.array_equal(Yp.view(np.uint32), Yw.view(np.uint32)), (rep, N, K)
+        assert split_counters_clear(ws, N, K), (rep, N, K)
 
 
 def test_columns_equal_single_token_calls():
