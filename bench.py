@@ -213,6 +213,90 @@ def time_graph_steps(layer: Layer, n_live: int, steps: int, warmup: int):
     return dt * 1e3 / steps, same, spg
 
 
+def run_schedule(layer: Layer, steps: int, warmup: int) -> dict:
+    """The workload's seeded decode schedule: `steps` steps whose live batch
+    is uniform on 1..16, each step's batch_index a random prefix of a slot
+    permutation, every step the whole hot path (each matrix: pre-quantise,
+    then the narrow matmul at that step's live batch) with the weight copies
+    rotated.  Reports the aggregate GB/s over the whole schedule (eager
+    launches, and one HIP graph of the whole schedule, checked bit-identical
+    to eager on its last step) and, per live batch, the number of steps and
+    their mean time from a pair of HIP events around every step."""
+    import torch
+    sched = wl.schedule(layer.w.config, steps)
+    bis = [torch.from_numpy(b).cuda() for b in sched]
+    ns = [int(b.size) for b in sched]
+    total = sum(step_bytes(layer.mats, n) for n in ns)
+
+    def run_all(events=None):
+        for s in range(steps):
+            if events is not None:
+                events[s][0].record()
+            layer.step(s % layer.copies, bis[s], ns[s])
+            if events is not None:
+                events[s][1].record()
+
+    for s in range(min(warmup, steps)):
+        layer.step(s % layer.copies, bis[s], ns[s])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run_all()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for s in range(layer.copies):
+            layer.step(s, bis[s], ns[s])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_all()
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_graph = e0.elapsed_time(e1)
+    got = [y.clone() for y in layer.Y]
+    layer.step((steps - 1) % layer.copies, bis[-1], ns[-1])
+    torch.cuda.synchronize()
+    same = all(torch.equal(a.view(torch.int32), b.view(torch.int32)) for a, b in zip(got, layer.Y))
+    del g
+
+    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+          for _ in range(steps)]
+    run_all(ev)
+    torch.cuda.synchronize()
+    per = {}
+    for n, (a, b) in zip(ns, ev):
+        per.setdefault(n, []).append(a.elapsed_time(b))
+    by_n = {}
+    for n in sorted(per):
+        t = float(np.mean(per[n]))
+        by_n[n] = {"steps": len(per[n]), "mean_us": round(t * 1e3, 2),
+                   "GBps": round(step_bytes(layer.mats, n) / (t * 1e-3) / 1e9, 1)}
+    ms = ms_graph if same and ms_graph < ms_eager else ms_eager
+    return {
+        "workload": layer.w.key, "matrices": {m.name: [m.K, m.N] for m in layer.mats},
+        "steps": steps, "schedule": "live batch uniform on 1..16, seeded random prefix of a slot "
+                                    "permutation per step",
+        "bytes": total, "value": round(total / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+        "frac_peak": round(total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "ms_total": round(ms, 4), "us_per_step": round(ms * 1e3 / steps, 2),
+        "ms_total_eager": round(ms_eager, 4), "ms_total_graph": round(ms_graph, 4),
+        "graph_bit_identical": same,
+        "timing": "one hip graph of the whole schedule" if ms is ms_graph else "eager launches",
+        "weight_copies_rotated": layer.copies,
+        "by_n_live": by_n,
+    }
+
+
 def graph_replay_us(launch, launches: int, replays: int) -> list:
     """Per-launch duration of each of `replays` replays of one HIP graph that
     holds `launches` back-to-back launches (launch(c) for c in
@@ -615,6 +699,9 @@ def main(argv=None) -> int:
                     help="skip the 16..64-column multi-token measurement")
     ap.add_argument("--engine-ab", action="store_true",
                     help="only time both dot engines on every matrix at n_live 1, 2, 4, 8, 16")
+    ap.add_argument("--schedule", type=int, default=0, metavar="STEPS",
+                    help="only run the workload's seeded decode schedule of this many steps "
+                         "(live batch uniform on 1..16): aggregate GB/s and per-live-batch times")
     args = ap.parse_args(argv)
 
     if args.pmc_summarize:
@@ -640,6 +727,14 @@ def main(argv=None) -> int:
     if args.engine_ab:
         res = engine_ab(layer, (1, 2, 4, 8, 16), max(16, 2 * layer.copies))
         text = json.dumps({"engine_ab": res, "workload": args.workload})
+        print(text, flush=True)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text + "\n")
+        return 0
+    if args.schedule:
+        res = run_schedule(layer, args.schedule, args.warmup)
+        text = json.dumps(res)
         print(text, flush=True)
         if args.out:
             with open(args.out, "w") as f:

@@ -58,3 +58,19 @@ def test_steps_per_graph_divides_the_timed_steps():
     for copies, steps in ((4, 400), (4, 100), (2, 30), (5, 7)):
         n = bench.steps_per_graph(copies, steps)
         assert steps % n == 0 and (n == 1 or n % copies == 0)
+
+
+def test_schedule_draws_every_live_batch_uniformly():
+    """The large dense shapes' 1000-step schedule: every live batch 1..16
+    occurs, each about 1000/16 times, and every step's batch_index is a
+    prefix of a slot permutation (distinct slots in 0..15)."""
+    import numpy as np
+    sched = wl.schedule(wl.WORKLOADS["large_dense"].config, 1000)
+    counts = np.bincount([b.size for b in sched], minlength=17)
+    assert counts[0] == 0 and counts[1:].sum() == 1000
+    assert counts[1:].min() >= 30 and counts[1:].max() <= 100
+    for b in sched:
+        assert b.dtype == np.int32 and len(set(b.tolist())) == b.size
+        assert b.min() >= 0 and b.max() < 16
+    bytes_total = sum(bench.step_bytes(wl.WORKLOADS["large_dense"].matrices, b.size) for b in sched)
+    assert bytes_total > 1000 * 2 * 140_000_000
