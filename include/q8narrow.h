@@ -35,7 +35,9 @@
  *     is not gfx950 gives Q8_ERR_UNSUPPORTED; a launch failure reported by
  *     the HIP runtime gives Q8_ERR_HIP.  The library never aborts.
  *   - Shapes: N >= 1 output features, K >= 32 input features with K % 32 == 0,
- *     N * K <= 2^40, K < 2^24.
+ *     K < 2^24, and the matrix padded to whole groups of 16 rows and 256
+ *     columns holds at most 2^34 values (17 GB packed; every launch then
+ *     stays below 2^32 threads).  Any other shape is an invalid argument.
  *   - Alignment: W, X, Wq, Xq 16 bytes; q 8 bytes; Y, batch_index 4 bytes;
  *     d16 2 bytes.  A null or misaligned pointer is an invalid argument.
  */
@@ -253,8 +255,8 @@ q8_status q8_matmul_multi(const void* Wq, const void* Xq, int n_slots,
  * to fp32.
  *
  * 1 <= n_rows <= Q8_MAX_COLUMNS; n_heads >= 1; head_dim even, 2..1024;
- * n_heads * head_dim <= row_stride; 1 < base < 1e30; Y and pos 4-byte
- * aligned. */
+ * n_heads * head_dim <= row_stride; n_rows * n_heads * head_dim <= 2^32;
+ * n_rows * row_stride <= 2^40; 1 < base < 1e30; Y and pos 4-byte aligned. */
 q8_status q8_rope_multi(float* Y, int n_rows, int64_t row_stride, const int32_t* pos,
                         int n_heads, int head_dim, double base, hipStream_t stream);
 

@@ -19,11 +19,15 @@
 namespace {
 
 constexpr int64_t kMaxK = int64_t(1) << 24;
-constexpr int64_t kMaxNK = int64_t(1) << 40;
+// Values of the matrix padded to whole row groups (16 rows) and super-chunks
+// (256 values).  The packer runs one thread per 8 padded values, and a
+// launch must stay below 2^32 threads; 2^34 values is 17 GB packed.
+constexpr int64_t kMaxPaddedNK = int64_t(1) << 34;
 
 bool valid_shape(int64_t N, int64_t K) {
-    return N >= 1 && K >= Q8_BLOCK && K % Q8_BLOCK == 0 && K < kMaxK &&
-           N <= kMaxNK / K;
+    if (N < 1 || K < Q8_BLOCK || K % Q8_BLOCK != 0 || K >= kMaxK) return false;
+    const int64_t Kp = (K + 255) / 256 * 256;
+    return N <= kMaxPaddedNK / Kp && (N + 15) / 16 * 16 <= kMaxPaddedNK / Kp;
 }
 
 bool valid_slots(int n_slots) {
@@ -206,7 +210,8 @@ q8_status q8_rope_multi(float* Y, int n_rows, int64_t row_stride, const int32_t*
                         int n_heads, int head_dim, double base, hipStream_t stream) {
     if (n_rows < 1 || n_rows > Q8_MAX_COLUMNS || n_heads < 1 || head_dim < 2 ||
         head_dim % 2 != 0 || head_dim > 1024 || row_stride < (int64_t)n_heads * head_dim ||
-        row_stride > (int64_t(1) << 40) / n_rows || !(base > 1.0) || !(base < 1e30) ||
+        row_stride > (int64_t(1) << 40) / n_rows ||
+        (int64_t)n_heads * head_dim > (int64_t(1) << 32) / n_rows || !(base > 1.0) || !(base < 1e30) ||
         !aligned(Y, 4) || !aligned(pos, 4))
         return Q8_ERR_INVALID_ARG;
     if (!current_device_ok()) return Q8_ERR_UNSUPPORTED;

@@ -79,6 +79,18 @@ def test_invalid_shapes_have_no_size(q8, N, K):
     assert q8.q8_packed_weight_bytes(N, K) == 0
 
 
+def test_shape_limit_is_the_padded_size(q8):
+    # the matrix padded to whole 16-row groups and 256-value super-chunks may
+    # hold 2^34 values (every launch then stays below 2^32 threads)
+    assert q8.q8_packed_weight_bytes(1 << 26, 256) == (1 << 26) * 256 * 34 // 32
+    assert q8.q8_packed_weight_bytes((1 << 26) + 1, 256) == 0   # pads to 2^26 + 16 rows
+    assert q8.q8_packed_weight_bytes(1 << 26, 32) > 0            # 32 values pad to 256
+    assert q8.q8_packed_weight_bytes((1 << 26) + 1, 32) == 0
+    assert q8.q8_packed_weight_bytes(1 << 13, (1 << 21) - 32) > 0
+    assert q8.q8_packed_weight_bytes((1 << 13) + 1, (1 << 21) - 32) == 0
+    assert q8.q8_packed_weight_bytes(151936, 5120) > 0           # the largest matrix here
+
+
 def test_invalid_k_has_no_slot_buffer(q8):
     assert q8.q8_act_buffer_bytes(0) == 0
     assert q8.q8_act_buffer_bytes(33) == 0
@@ -241,6 +253,9 @@ def test_rope_rejects_invalid_arguments(q8):
     assert call(6, 1.0) == bad and call(6, float("nan")) == bad and call(6, -5.0) == bad
     assert call(0, None) == bad and call(0, P + 2) == bad    # Y null, misaligned
     assert call(3, None) == bad and call(3, P + 1) == bad    # pos null, misaligned
+    # more than 2^32 rotated values (the launch would pass 2^32 threads)
+    a = [P, 64, 65537 * 1024, P, 65537, 1024, 1e6, None]
+    assert lib.q8_rope_multi(*a) == bad
 
 
 def test_stream_read_rejects_invalid_arguments(q8):
