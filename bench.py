@@ -475,6 +475,51 @@ def cpu_baseline(key: str, n_live: int, seconds: float = 10.0):
     }
 
 
+def cpu_detail(key: str, runs: int = 3) -> dict:
+    """The oracle as it stands, per matrix of the workload: its matmul at
+    n_live 1 and 16, on all the host threads OpenMP uses and on one, each the
+    median wall time of `runs` runs; and its pre-quantisation of the 16 slots
+    per K, timed separately (all threads)."""
+    import oracle
+    orc = oracle.get()
+    w = wl.WORKLOADS[key]
+    all_threads = orc.num_threads()
+    out = {"workload": key, "threads_all": all_threads, "runs": runs, "matrices": {},
+           "quantize": {}}
+    for i, m in enumerate(w.matrices):
+        qw, dw = orc.quantize_rows(wl.weights(w.config, i, m.N, m.K))
+        X = wl.activations(w.config, m.K, outliers=w.outliers)
+        qx, dx = orc.quantize_rows(X)
+        rec = {}
+        for threads in (all_threads, 1):
+            orc.set_num_threads(threads)
+            for n in (1, 16):
+                bi = wl.batch_index(w.config, n, random=w.random_batch_index)
+                ts = []
+                for _ in range(runs):
+                    t0 = time.perf_counter()
+                    orc.matmul(qw, dw, qx, dx, bi)
+                    ts.append(time.perf_counter() - t0)
+                t = float(np.median(ts))
+                rec[f"threads={threads} n_live={n}"] = {
+                    "ms": round(t * 1e3, 2), "GBps": round(matmul_bytes(m.N, m.K, n) / t / 1e9, 4)}
+            print(f"# oracle {m.name} threads={threads}: "
+                  + ", ".join(f"{k.split()[1]} {v['ms']} ms" for k, v in rec.items()
+                              if k.startswith(f"threads={threads} ")), file=sys.stderr, flush=True)
+        orc.set_num_threads(all_threads)
+        out["matrices"][m.name] = {"K": m.K, "N": m.N, **rec}
+        if m.K not in out["quantize"]:
+            ts = []
+            for _ in range(runs):
+                t0 = time.perf_counter()
+                orc.quantize_rows(X)
+                ts.append(time.perf_counter() - t0)
+            t = float(np.median(ts))
+            out["quantize"][m.K] = {"ms": round(t * 1e3, 3),
+                                    "GBps": round(quantize_bytes(m.K) / t / 1e9, 4)}
+    return out
+
+
 # ------------------------------------------------------------- profiles
 
 def kernel_source_hash() -> str:
@@ -699,6 +744,9 @@ def main(argv=None) -> int:
                     help="skip the 16..64-column multi-token measurement")
     ap.add_argument("--engine-ab", action="store_true",
                     help="only time both dot engines on every matrix at n_live 1, 2, 4, 8, 16")
+    ap.add_argument("--cpu-detail", action="store_true",
+                    help="only time the CPU oracle per matrix at n_live 1 and 16, on all host "
+                         "threads and on one (median of 3), and its pre-quantisation")
     ap.add_argument("--schedule", type=int, default=0, metavar="STEPS",
                     help="only run the workload's seeded decode schedule of this many steps "
                          "(live batch uniform on 1..16): aggregate GB/s and per-live-batch times")
@@ -716,6 +764,15 @@ def main(argv=None) -> int:
     if not 1 <= args.n_live <= 16:
         print("--n-live must be in 1..16", file=sys.stderr)
         return 2
+
+    if args.cpu_detail:
+        res = cpu_detail(args.workload)
+        text = json.dumps(res)
+        print(text, flush=True)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text + "\n")
+        return 0
 
     import torch
     torch.cuda.set_device(0)
