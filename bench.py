@@ -43,7 +43,7 @@ import workloads as wl  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, vendor figure
 COLD_BYTES = 1 << 30    # rotate weight copies past 1 GiB
-DOMINANT = "gate_up"
+PMC_WORKLOAD, PMC_MATRIX = "qwen3_layer", "gate_up"  # what the counter probe runs
 STEP_REPEATS = 11       # windows for the step time's median and p90
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -535,9 +535,10 @@ def pmc_summary_path(fused: bool) -> str:
     return os.path.join(PROFILE_DIR, name)
 
 
-def measured_traffic(n_live: int, fused: bool):
-    """HBM bytes per launch of the dominant kernel from the committed PMC
-    counter summary, if it was taken on the current kernel source."""
+def measured_traffic(workload: str, matrix: str, n_live: int, fused: bool):
+    """HBM bytes per launch of this workload's matrix from the committed PMC
+    counter summary, if the summary covers that matrix and was taken on the
+    current kernel source."""
     path = pmc_summary_path(fused)
     try:
         with open(path) as f:
@@ -545,6 +546,8 @@ def measured_traffic(n_live: int, fused: bool):
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    if rec.get("workload") != workload or rec.get("matrix") != matrix:
         return None
     per = rec.get("traffic_bytes_per_launch", {}).get(str(n_live))
     return None if per is None else int(per)
@@ -585,26 +588,29 @@ def multi_columns(layer: Layer, widths, launches: int) -> dict:
 
 # ------------------------------------------------------ pos-vector RoPE
 
-ROPE_HEADS, ROPE_HEAD_DIM, ROPE_BASE = 48, 128, 1e6  # Qwen3-14B: 40 query + 8 key heads
 
 
 def rope_after_qkv(layer: Layer, n_live: int, launches: int = 100):
-    """The pos-vector RoPE on the QKV matmul's output rows (the query and key
-    heads of the Qwen3-14B layer, one position per live token): average
-    launch duration and algorithmic GB/s (each rotated value read and written
-    once in fp32, plus the positions)."""
+    """The pos-vector RoPE on the QKV matmul's output rows (the workload's
+    query and key heads, e.g. 40 + 8 heads of 128 on the Qwen3-14B layer, one
+    position per live token): average launch duration and algorithmic GB/s
+    (each rotated value read and written once in fp32, plus the positions).
+    None for a workload without a QKV matrix or a RoPE configuration."""
     import torch
     q8 = layer.q8
     i = [k for k, m in enumerate(layer.mats) if m.name == "qkv"]
-    if not i:
+    if not i or layer.w.rope is None:
         return None
+    heads, head_dim, base = layer.w.rope
     m = layer.mats[i[0]]
+    if heads * head_dim > m.N:
+        return None
     pos = torch.arange(1000, 1000 + n_live, dtype=torch.int32, device="cuda") * 37
-    us = graph_avg_us(lambda c: q8.q8_rope_multi(layer.Y[i[0]], n_live, m.N, pos, ROPE_HEADS,
-                                                 ROPE_HEAD_DIM, ROPE_BASE), launches)
-    nbytes = 2 * 4 * n_live * ROPE_HEADS * ROPE_HEAD_DIM + 4 * n_live
+    us = graph_avg_us(lambda c: q8.q8_rope_multi(layer.Y[i[0]], n_live, m.N, pos, heads,
+                                                 head_dim, base), launches)
+    nbytes = 2 * 4 * n_live * heads * head_dim + 4 * n_live
     return {"us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1), "rows": n_live,
-            "heads": ROPE_HEADS, "head_dim": ROPE_HEAD_DIM, "base": ROPE_BASE}
+            "heads": heads, "head_dim": head_dim, "base": base}
 
 
 # ------------------------------------------------------- engine A/B
@@ -651,8 +657,8 @@ def pmc_probe(launches: int, n_live: int, fused: bool) -> None:
     weight copies, then the calibration copy three times."""
     import torch
     import quantized_weight_streaming_q8_amd as q8
-    w = wl.WORKLOADS["qwen3_layer"]
-    i = [k for k, m in enumerate(w.matrices) if m.name == DOMINANT][0]
+    w = wl.WORKLOADS[PMC_WORKLOAD]
+    i = [k for k, m in enumerate(w.matrices) if m.name == PMC_MATRIX][0]
     m = w.matrices[i]
     W = torch.from_numpy(wl.weights(w.config, i, m.N, m.K)).cuda()
     packed = [q8.empty_packed_weights(m.N, m.K) for _ in range(2)]
@@ -691,7 +697,8 @@ def _counter_rows(path: str, counter: str):
 def pmc_summarize(fetch_csv: str, write_csv: str, n_live: int, fused: bool, out: str) -> dict:
     """Per-launch HBM bytes of the dominant kernel from the two counter
     passes, each scaled by the calibration copy."""
-    res = {"kernel_source_hash": kernel_source_hash(), "n_live": n_live, "fused": fused,
+    res = {"kernel_source_hash": kernel_source_hash(), "workload": PMC_WORKLOAD,
+           "matrix": PMC_MATRIX, "n_live": n_live, "fused": fused,
            "calibration_copy_bytes": CAL_BYTES}
     per = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -853,9 +860,9 @@ def main(argv=None) -> int:
     print("# fused pre-quantise + matmul: "
           + ", ".join(f"{m.name} {u:.2f} us" for m, u in zip(mats, fused_us)), file=sys.stderr, flush=True)
 
-    # roofline of the dominant kernel of the step as run
-    dom = [i for i, m in enumerate(mats) if m.name == DOMINANT]
-    di = dom[0] if dom else int(np.argmax([m.N * m.K for m in mats]))
+    # roofline of the dominant kernel of the step as run: the largest
+    # matrix's (gate+up on the Qwen3-14B layer)
+    di = int(np.argmax([m.N * m.K for m in mats]))
     dm = mats[di]
     dom_bytes = matmul_bytes(dm.N, dm.K, args.n_live) + (quantize_bytes(dm.K) if args.fused else 0)
     dom_us = fused_us[di] if args.fused else kern_us[di]
@@ -863,7 +870,7 @@ def main(argv=None) -> int:
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
         "frac": round(achieved / PEAK_HBM_GBS, 4),
-        "traffic": measured_traffic(args.n_live, args.fused),
+        "traffic": measured_traffic(args.workload, dm.name, args.n_live, args.fused),
         "kernel": (f"fused pre-quantise + q8 narrow matmul" if args.fused else "q8 narrow matmul")
         + f", {dm.name} {dm.K}->{dm.N}, n_live={args.n_live}",
         "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 2),
@@ -898,7 +905,7 @@ def main(argv=None) -> int:
     copy_gbs = copy_ceiling_gbs()
     read_gbs = read_ceiling_gbs(layer.q8)
     print(f"# read ceiling (plain streaming read of 2 GiB): {read_gbs:.0f} GB/s; "
-          f"gate+up at {roofline['achieved'] / read_gbs:.0%} of it", file=sys.stderr, flush=True)
+          f"{dm.name} at {roofline['achieved'] / read_gbs:.0%} of it", file=sys.stderr, flush=True)
     # the spread of the step time: STEP_REPEATS more windows of as many eager
     # steps as the timed run, each between two device synchronisations
     layer.fused = args.fused

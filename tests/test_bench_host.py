@@ -74,3 +74,27 @@ def test_schedule_draws_every_live_batch_uniformly():
         assert b.min() >= 0 and b.max() < 16
     bytes_total = sum(bench.step_bytes(wl.WORKLOADS["large_dense"].matrices, b.size) for b in sched)
     assert bytes_total > 1000 * 2 * 140_000_000
+
+
+def test_rope_configurations_fit_their_qkv_rows():
+    """Each workload's pos-vector RoPE heads (query + key) fit the QKV
+    matrix's output rows; Qwen3-14B rotates 40 + 8 heads of 128."""
+    for key, w in wl.WORKLOADS.items():
+        if w.rope is None:
+            continue
+        heads, head_dim, base = w.rope
+        qkv = [m for m in w.matrices if m.name == "qkv"]
+        assert qkv, key
+        assert head_dim % 2 == 0 and heads * head_dim <= qkv[0].N and base > 1, key
+    assert wl.WORKLOADS["qwen3_layer"].rope == (48, 128, 1e6)
+
+
+def test_traffic_is_reported_only_for_the_matrix_it_was_counted_on():
+    """The committed counter summary covers the Qwen3-14B layer's gate+up:
+    no other workload or matrix borrows its traffic."""
+    assert bench.measured_traffic("qwen3_head", "head", 16, False) is None
+    assert bench.measured_traffic("qwen3_layer", "down", 16, False) is None
+    t = bench.measured_traffic("qwen3_layer", "gate_up", 16, False)
+    if t is not None:  # only while the summary matches the kernel source
+        alg = bench.matmul_bytes(34816, 5120, 16)
+        assert alg <= t <= 1.05 * alg

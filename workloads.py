@@ -53,6 +53,9 @@ class Workload:
     n_live: tuple
     outliers: bool = False
     random_batch_index: bool = False
+    # pos-vector RoPE on the QKV output: (rotated heads, head_dim, base), the
+    # query and key heads that lead the QKV rows; None where there is none
+    rope: tuple | None = None
 
 
 WORKLOADS = {
@@ -62,12 +65,12 @@ WORKLOADS = {
         (Matrix("qkv", 768, 2304), Matrix("o", 768, 768),
          Matrix("gate_up", 768, 6144), Matrix("down", 3072, 768),
          Matrix("head", 768, 32000)),
-        (1, 2, 4, 8)),
+        (1, 2, 4, 8), rope=(24, 64, 1e4)),
     "qwen3_layer": Workload(
         "qwen3_layer", 3,
         (Matrix("qkv", 5120, 7168), Matrix("o", 5120, 5120),
          Matrix("gate_up", 5120, 34816), Matrix("down", 17408, 5120)),
-        tuple(range(1, 17)), outliers=True, random_batch_index=True),
+        tuple(range(1, 17)), outliers=True, random_batch_index=True, rope=(48, 128, 1e6)),
     "qwen3_head": Workload(
         "qwen3_head", 4, (Matrix("head", 5120, 151936),), (1, 2, 4, 8, 16)),
     "large_dense": Workload(
