@@ -43,7 +43,6 @@ import workloads as wl  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, vendor figure
 COLD_BYTES = 1 << 30    # rotate weight copies past 1 GiB
-PMC_WORKLOAD, PMC_MATRIX = "qwen3_layer", "gate_up"  # what the counter probe runs
 STEP_REPEATS = 11       # windows for the step time's median and p90
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -530,8 +529,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def pmc_summary_path(fused: bool) -> str:
-    name = "gate_up_fused_qwen3_layer_pmc.json" if fused else "gate_up_matmul_qwen3_layer_pmc.json"
+def dominant_matrix(key: str) -> int:
+    """Index of a workload's dominant matrix: the largest (gate+up on the
+    Qwen3-14B layer)."""
+    return int(np.argmax([m.N * m.K for m in wl.WORKLOADS[key].matrices]))
+
+
+def pmc_summary_path(workload: str, matrix: str, fused: bool) -> str:
+    name = f"{matrix}_{'fused' if fused else 'matmul'}_{workload}_pmc.json"
     return os.path.join(PROFILE_DIR, name)
 
 
@@ -539,7 +544,7 @@ def measured_traffic(workload: str, matrix: str, n_live: int, fused: bool):
     """HBM bytes per launch of this workload's matrix from the committed PMC
     counter summary, if the summary covers that matrix and was taken on the
     current kernel source."""
-    path = pmc_summary_path(fused)
+    path = pmc_summary_path(workload, matrix, fused)
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -651,14 +656,14 @@ def engine_ab(layer: Layer, n_values, launches: int) -> dict:
 CAL_BYTES = 256 << 20
 
 
-def pmc_probe(launches: int, n_live: int, fused: bool) -> None:
-    """The dominant kernel of the Layer workload's step (the fused
-    pre-quantise + matmul, or the matmul alone), `launches` times over two
-    weight copies, then the calibration copy three times."""
+def pmc_probe(key: str, launches: int, n_live: int, fused: bool) -> None:
+    """The dominant kernel of the workload's step (the fused pre-quantise +
+    matmul, or the matmul alone), `launches` times over two weight copies,
+    then the calibration copy three times."""
     import torch
     import quantized_weight_streaming_q8_amd as q8
-    w = wl.WORKLOADS[PMC_WORKLOAD]
-    i = [k for k, m in enumerate(w.matrices) if m.name == PMC_MATRIX][0]
+    w = wl.WORKLOADS[key]
+    i = dominant_matrix(key)
     m = w.matrices[i]
     W = torch.from_numpy(wl.weights(w.config, i, m.N, m.K)).cuda()
     packed = [q8.empty_packed_weights(m.N, m.K) for _ in range(2)]
@@ -694,11 +699,13 @@ def _counter_rows(path: str, counter: str):
         return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
 
 
-def pmc_summarize(fetch_csv: str, write_csv: str, n_live: int, fused: bool, out: str) -> dict:
-    """Per-launch HBM bytes of the dominant kernel from the two counter
-    passes, each scaled by the calibration copy."""
-    res = {"kernel_source_hash": kernel_source_hash(), "workload": PMC_WORKLOAD,
-           "matrix": PMC_MATRIX, "n_live": n_live, "fused": fused,
+def pmc_summarize(fetch_csv: str, write_csv: str, key: str, n_live: int, fused: bool,
+                  out: str) -> dict:
+    """Per-launch HBM bytes of the workload's dominant kernel from the two
+    counter passes, each scaled by the calibration copy."""
+    res = {"kernel_source_hash": kernel_source_hash(), "workload": key,
+           "matrix": wl.WORKLOADS[key].matrices[dominant_matrix(key)].name,
+           "n_live": n_live, "fused": fused,
            "calibration_copy_bytes": CAL_BYTES}
     per = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -760,8 +767,11 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.pmc_summarize:
-        path = pmc_summary_path(args.fused)
-        print(json.dumps(pmc_summarize(*args.pmc_summarize, args.n_live, args.fused, path), indent=1))
+        path = pmc_summary_path(args.workload,
+                                wl.WORKLOADS[args.workload].matrices[dominant_matrix(args.workload)].name,
+                                args.fused)
+        print(json.dumps(pmc_summarize(*args.pmc_summarize, args.workload, args.n_live, args.fused,
+                                       path), indent=1))
         return 0
 
     if args.gpus != 1:
@@ -784,7 +794,7 @@ def main(argv=None) -> int:
     import torch
     torch.cuda.set_device(0)
     if args.pmc_probe:
-        pmc_probe(args.pmc_probe, args.n_live, args.fused)
+        pmc_probe(args.workload, args.pmc_probe, args.n_live, args.fused)
         return 0
     layer = Layer(args.workload, fused=args.fused)
     mats = layer.mats
@@ -860,9 +870,8 @@ def main(argv=None) -> int:
     print("# fused pre-quantise + matmul: "
           + ", ".join(f"{m.name} {u:.2f} us" for m, u in zip(mats, fused_us)), file=sys.stderr, flush=True)
 
-    # roofline of the dominant kernel of the step as run: the largest
-    # matrix's (gate+up on the Qwen3-14B layer)
-    di = int(np.argmax([m.N * m.K for m in mats]))
+    # roofline of the dominant kernel of the step as run
+    di = dominant_matrix(args.workload)
     dm = mats[di]
     dom_bytes = matmul_bytes(dm.N, dm.K, args.n_live) + (quantize_bytes(dm.K) if args.fused else 0)
     dom_us = fused_us[di] if args.fused else kern_us[di]
