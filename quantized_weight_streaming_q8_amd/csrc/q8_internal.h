@@ -105,21 +105,24 @@ __device__ inline int64_t packed_d_index(int64_t row, int64_t blk, int64_t NSC) 
 
 // ------------------------------------------------------------------------
 // q8_0 quantisation of one 8-value segment by a group of 4 lanes that
-// together hold a 32-value block.  Lanes of the group must be 4 consecutive
-// lanes starting at a multiple of 4 and all of them must be active.
+// together hold a 32-value block: lanes l, l ^ L, l ^ 2L and l ^ 3L (L = 1:
+// 4 consecutive lanes starting at a multiple of 4; L = 16: lanes 16 apart).
+// All of them must be active.
 // ------------------------------------------------------------------------
 struct QuantSeg {
     uint32_t lo, hi;  // 8 int8 values, little-endian
     uint16_t d16;     // binary16 scale of the block
 };
 
+template <int L = 1>
 __device__ inline QuantSeg quantize_segment(const float v[8]) {
+    static_assert(L == 1 || L == 16, "lane distance of a block's segments");
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
     // absmax of the 32-value block across the 4-lane group (max is exact)
-    a = fmaxf(a, __shfl_xor(a, 1, 4));
-    a = fmaxf(a, __shfl_xor(a, 2, 4));
+    a = fmaxf(a, __shfl_xor(a, L, 4 * L));
+    a = fmaxf(a, __shfl_xor(a, 2 * L, 4 * L));
     QuantSeg r;
     if (a == 0.0f) {
         r.lo = r.hi = 0u;

@@ -9,9 +9,16 @@
 // An activation slot buffer of n_slots slots uses the packed layout of an
 // n_slots-row matrix (row = slot).
 //
-// Thread mapping, all kernels: one lane per 8-value segment, 4 consecutive
-// lanes per 32-value block, consecutive blocks of a row on consecutive lane
-// groups, so a wave reads 2 KB of contiguous fp32 per row.
+// Thread mapping.  The weight packer: one wave per chunk of the packed
+// layout (16 rows x 2 blocks, 1 KB), lane l holding exactly the 16 bytes it
+// stores at l*16: row l & 15, k-slot l >> 4, 8 values of each of the two
+// blocks.  Every wave's q store is one contiguous 1 KB and its scale store
+// 64 contiguous bytes; a block's 4 segments sit in lanes 16 apart.  The
+// activation pre-quantiser, import and export: one lane per 8-value
+// segment, 4 consecutive lanes per block, consecutive blocks of a row on
+// consecutive lane groups, so a wave reads 2 KB of contiguous fp32 per row
+// (on the 16 short rows of the slots, twice the waves of the packer's
+// mapping and longer contiguous reads: measured faster there).
 
 #include "q8_internal.h"
 
@@ -42,19 +49,36 @@ __device__ inline void load8(const float* p, float v[8]) {
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// Quantise rows [16g, 16g+16) x blocks [2cg, 2cg+2) of the row-major fp32
+// W (N x K) into chunk cg of row group g of the packed layout.  Rows past N
+// and blocks past K are written as zeros, the layout's padding.
 __global__ void __launch_bounds__(kThreads)
-pack_weights_kernel(const float* __restrict__ W, int64_t N, int64_t K,
-                    int64_t KB, int64_t NSC, int64_t total,
-                    uint8_t* __restrict__ wq, uint16_t* __restrict__ wd) {
-    const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (tid >= total) return;  // total is a multiple of 4: groups exit whole
-    const SegIndex ix = seg_index(tid, NSC * kScBlocks);
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (ix.row < N && ix.blk < KB) load8(W + ix.row * K + ix.blk * kBlock + ix.seg * 8, v);
-    const QuantSeg r = quantize_segment(v);
-    *reinterpret_cast<uint2*>(wq + packed_q_offset(ix.row, ix.blk, ix.seg, NSC)) =
-        make_uint2(r.lo, r.hi);
-    if (ix.seg == 0) wd[packed_d_index(ix.row, ix.blk, NSC)] = r.d16;
+pack_weights_kernel(const float* __restrict__ W, int64_t N, int64_t K, int64_t KB,
+                    int64_t NSC, int64_t n_waves, uint8_t* __restrict__ wq,
+                    uint16_t* __restrict__ wd) {
+    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (wave >= n_waves) return;  // wave-uniform
+    const int lane = threadIdx.x & 63;
+    const int64_t chunks = NSC * 4;
+    const int64_t g = wave / chunks, cg = wave % chunks;
+    const int64_t row = g * kRowsPerGroup + (lane & 15);
+    const int ks = lane >> 4;
+    uint32_t out[4];
+    uint32_t dd = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t blk = 2 * cg + h;
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (row < N && blk < KB) load8(W + row * K + blk * kBlock + slot_pos(ks), v);
+        const QuantSeg r = quantize_segment<16>(v);
+        out[2 * h] = r.lo;
+        out[2 * h + 1] = r.hi;
+        dd |= (uint32_t)r.d16 << (16 * h);
+    }
+    *reinterpret_cast<uint4*>(wq + (g * chunks + cg) * kChunkBytes + lane * 16) =
+        make_uint4(out[0], out[1], out[2], out[3]);
+    if (ks == 0)  // blocks 2cg and 2cg+1 of this row: scale halves 2j, 2j+1 of the chunk
+        *reinterpret_cast<uint32_t*>(wd + ((g * chunks + cg) * kRowsPerGroup + (lane & 15)) * 2) = dd;
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -113,10 +137,10 @@ inline unsigned grid_for(int64_t total) {
 
 hipError_t launch_pack_weights(const float* W, const Shape& s, uint8_t* Wq,
                                hipStream_t st) {
-    const int64_t total = s.G * kRowsPerGroup * s.NSC * kScBlocks * 4;
+    const int64_t waves = s.G * s.NSC * 4;  // one per chunk
     uint16_t* wd = reinterpret_cast<uint16_t*>(Wq + s.q_bytes);
-    hipLaunchKernelGGL(pack_weights_kernel, dim3(grid_for(total)), dim3(kThreads),
-                       0, st, W, s.N, s.K, s.KB, s.NSC, total, Wq, wd);
+    hipLaunchKernelGGL(pack_weights_kernel, dim3(grid_for(waves * 64)), dim3(kThreads),
+                       0, st, W, s.N, s.K, s.KB, s.NSC, waves, Wq, wd);
     return hipGetLastError();
 }
 
