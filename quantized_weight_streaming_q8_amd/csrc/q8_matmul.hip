@@ -130,7 +130,7 @@ struct MmArgs {
     uint32_t* qready;     // kReadyCopies "slots published" flags, kReadyStride apart
 };
 
-// Super-chunk range [lo, hi) of wave slice k of split s (NSC < 2^16, so 32-bit
+// Super-chunk range [lo, hi) of wave slice k of split s (NSC <= 2^16, so 32-bit
 // products are exact).
 __device__ inline void slice_range(int NSC, int S, int KW, int s, int k, int& lo, int& hi) {
     const int s0 = s * NSC / S, s1 = (s + 1) * NSC / S;

@@ -183,6 +183,44 @@ def test_matmul_large_ragged_shapes(N, K):
     torch.cuda.empty_cache()
 
 
+def test_largest_k():
+    """The largest K the boundary takes, 2^24 - 32: 65536 super-chunks, the
+    last of them 7 blocks long, split 4 ways across workgroups; N = 17 (a
+    ragged second row group).  Packed weights and slots bit-exact, outputs
+    within tolerance of the oracle, and the plain, workspace and DOT4
+    paths bit-identical.  (Each wave here adds ~131k terms in order, past
+    the length for which the tolerance bounds every order; the error of
+    these sums stays far inside it all the same.)"""
+    import quantized_weight_streaming_q8_amd as q8
+    N, K = 17, (1 << 24) - 32
+    assert q8.q8_packed_weight_bytes(N, K) > 0 and q8.q8_matmul_workspace_bytes(N, K) > 0
+    rng = np.random.default_rng(2024)
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    X = rng.standard_normal((16, K), dtype=np.float32)
+    Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
+    qw, dw = oracle.quantize_rows(W)
+    qx, dx = oracle.quantize_rows(X)
+    q, d = gpu_unpack(Wq, N, K)
+    assert np.array_equal(q, qw) and np.array_equal(d, dw)
+    del q, d
+    qs, ds = slots_host(Xq, K)
+    assert np.array_equal(qs, qx) and np.array_equal(ds, dx)
+    del qs, ds
+    ws = q8.zeroed_workspace(N, K)
+    for bi in (rng.permutation(16), np.array([9, 0, 9])):
+        bi = bi.astype(np.int32)
+        Yo, Ao = oracle.matmul(qw, dw, qx, dx, bi)
+        Ym = gpu_matmul(Wq, Xq, bi, N, K, MFMA)
+        ok, worst = within_tau(Ym, Yo, Ao)
+        assert ok, (bi, worst)
+        Yw = gpu_matmul_ws(Wq, Xq, bi, N, K, ws)
+        assert np.array_equal(Ym.view(np.uint32), Yw.view(np.uint32)), bi
+        Yd = gpu_matmul(Wq, Xq, bi, N, K, DOT4)
+        assert np.array_equal(Ym.view(np.uint32), Yd.view(np.uint32)), bi
+    del Wq, Xq, ws
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("n_live", [1, 2, 4])
 def test_single_768(n_live):
     w = wl.WORKLOADS["single"]
