@@ -221,6 +221,44 @@ def test_largest_k():
     torch.cuda.empty_cache()
 
 
+def test_largest_n():
+    """The most rows the boundary takes at K = 32, 2^26: K pads to one
+    256-value super-chunk, so the padded matrix holds the limit of 2^34
+    values (an 18 GB packed buffer, 2^31 threads to pack it, 2^21
+    workgroups to stream it).  The weights come in as canonical q8_0
+    (random codes, fp16 scales); sampled rows, the first and the last
+    included, are checked against the oracle on the device's outputs, and
+    the DOT4 engine must give the same bits."""
+    import quantized_weight_streaming_q8_amd as q8
+    N, K = 1 << 26, 32
+    assert q8.q8_packed_weight_bytes(N, K) > 0 and q8.q8_packed_weight_bytes(N + 1, K) == 0
+    rng = np.random.default_rng(26)
+    q = rng.integers(-127, 128, size=(N, K), dtype=np.int8)
+    d16 = rng.uniform(1e-4, 1e-3, size=(N, 1)).astype(np.float16).view(np.uint16)
+    Wq = gpu_pack_q(q, d16)
+    X = rng.standard_normal((16, K), dtype=np.float32)
+    Xq = gpu_quantize_acts(X)
+    qx, dx = oracle.quantize_rows(X)
+    rows = sample_rows(N, 96, seed=26)
+    rows_d = torch.from_numpy(rows).cuda()
+    for bi in (rng.permutation(16), np.array([4])):
+        bi = bi.astype(np.int32)
+        bi_d = to_dev(bi)
+        Y = torch.empty((bi.size, N), dtype=torch.float32, device="cuda")
+        q8.q8_matmul_narrow(Wq, Xq, bi_d, bi.size, N, K, Y)
+        Yd = torch.empty_like(Y)
+        q8.q8_matmul_narrow_path(Wq, Xq, bi_d, bi.size, N, K, Yd, DOT4)
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(torch.int32), Yd.view(torch.int32)), bi
+        Ys = Y[:, rows_d].cpu().numpy()
+        Yo, Ao = oracle.matmul(q, d16, qx, dx, bi, rows)
+        ok, worst = within_tau(Ys, Yo, Ao)
+        assert ok, (bi, worst)
+        del Y, Yd
+    del Wq
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("n_live", [1, 2, 4])
 def test_single_768(n_live):
     w = wl.WORKLOADS["single"]
