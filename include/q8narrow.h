@@ -61,7 +61,8 @@ typedef enum q8_status {
     Q8_OK = 0,
     Q8_ERR_INVALID_ARG = 1,
     Q8_ERR_UNSUPPORTED = 2,
-    Q8_ERR_HIP = 3
+    Q8_ERR_HIP = 3,
+    Q8_ERR_TOO_LARGE = 4 /* the shape needs more than a fixed buffer holds */
 } q8_status;
 
 /* Which int8 dot engine the matmul uses (all give bit-identical Y). */
@@ -173,6 +174,35 @@ q8_status q8_matmul_narrow_ws(const void* Wq, const void* Xq,
                               const int32_t* batch_index, int n_live,
                               int64_t N, int64_t K, float* Y, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/* ----------------------------------------------- no-allocation variant */
+
+/* Bytes of the device array behind q8_matmul_narrow_noalloc (8 MiB). */
+#define Q8_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/* For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Computes exactly what q8_matmul_narrow_ws computes (the same
+ * kernels, the same bits), with the workspace taken from a static device
+ * array of Q8_NOALLOC_SCRATCH_BYTES that the library holds on every device
+ * it runs on until the process ends.  The call allocates nothing: no
+ * hipMalloc, no hipFree, no allocating library routine.
+ *
+ * Limit: shapes whose q8_matmul_workspace_bytes(N, K) exceeds
+ * Q8_NOALLOC_SCRATCH_BYTES return Q8_ERR_TOO_LARGE and enqueue nothing
+ * (8 MiB holds the split records of up to 1927 row groups of 16 rows, i.e.
+ * N <= 30832 for the long rows that are split; shorter rows need none).
+ *
+ * The first call on a device takes the array's device address and enqueues
+ * a small kernel on `stream` that zero-fills it; make that first call
+ * outside stream capture.  Every completed call leaves the array ready for
+ * the next, on any shape.  All calls on one device share the one array: calls
+ * that can run at the same time on one device (other streams, other host
+ * threads without ordering) race and give wrong results; calls ordered on
+ * one stream are fine.  Other arguments and errors as q8_matmul_narrow. */
+q8_status q8_matmul_narrow_noalloc(const void* Wq, const void* Xq,
+                                   const int32_t* batch_index, int n_live, int64_t N,
+                                   int64_t K, float* Y, hipStream_t stream);
 
 /* ------------------------------------------- fused pre-quantisation */
 

@@ -27,6 +27,8 @@ Q8_OK = 0
 Q8_ERR_INVALID_ARG = 1
 Q8_ERR_UNSUPPORTED = 2
 Q8_ERR_HIP = 3
+Q8_ERR_TOO_LARGE = 4
+Q8_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 Q8_PATH_AUTO = 0
 Q8_PATH_MFMA = 1
@@ -45,6 +47,7 @@ _SIGNATURES = {
     "q8_matmul_narrow_path": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp, _i32], _i32),
     "q8_matmul_workspace_bytes": ([_i64, _i64], ctypes.c_size_t),
     "q8_matmul_narrow_ws": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp], _i32),
+    "q8_matmul_narrow_noalloc": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp], _i32),
     "q8_matmul_fused_workspace_bytes": ([_i64, _i64], ctypes.c_size_t),
     "q8_matmul_narrow_fused": ([_vp, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _vp, _vp,
                                 ctypes.c_size_t, _vp], _i32),
@@ -174,6 +177,13 @@ def q8_matmul_narrow_ws(Wq, Xq, batch_index, n_live: int, N: int, K: int, Y,
     _check(_lib.q8_matmul_narrow_ws(_ptr(Wq), _ptr(Xq), _ptr(batch_index), n_live, N, K,
                                     _ptr(Y), _ptr(workspace), workspace_bytes, _stream(stream)),
            "q8_matmul_narrow_ws")
+
+
+def q8_matmul_narrow_noalloc(Wq, Xq, batch_index, n_live: int, N: int, K: int, Y,
+                             stream=None) -> None:
+    _check(_lib.q8_matmul_narrow_noalloc(_ptr(Wq), _ptr(Xq), _ptr(batch_index), n_live, N, K,
+                                         _ptr(Y), _stream(stream)),
+           "q8_matmul_narrow_noalloc")
 
 
 def q8_matmul_fused_workspace_bytes(N: int, K: int) -> int:

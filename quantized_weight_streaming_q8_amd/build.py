@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libq8narrow.so")
 
-SOURCES = ["q8_pack.hip", "q8_matmul.hip", "q8_rope.hip", "q8_measure.hip", "q8_abi.hip"]
+SOURCES = ["q8_pack.hip", "q8_matmul.hip", "q8_rope.hip", "q8_measure.hip", "q8_abi.hip",
+           "q8_noalloc.hip"]
 HEADERS = ["q8_internal.h", "q8_measure.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

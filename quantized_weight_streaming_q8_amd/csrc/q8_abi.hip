@@ -61,6 +61,16 @@ q8_status from_hip(hipError_t e) { return e == hipSuccess ? Q8_OK : Q8_ERR_HIP; 
 
 }  // namespace
 
+namespace q8 {
+
+bool matmul_args_ok(const void* Wq, const void* Xq, const int32_t* batch_index, int n_live,
+                    int64_t N, int64_t K, const float* Y) {
+    return valid_shape(N, K) && n_live >= 1 && n_live <= Q8_MAX_SLOTS && aligned(Wq, 16) &&
+           aligned(Xq, 16) && aligned(batch_index, 4) && aligned(Y, 4);
+}
+
+}  // namespace q8
+
 extern "C" {
 
 size_t q8_packed_weight_bytes(int64_t N, int64_t K) {
@@ -124,9 +134,7 @@ q8_status q8_matmul_narrow_path(const void* Wq, const void* Xq,
                                 const int32_t* batch_index, int n_live,
                                 int64_t N, int64_t K, float* Y,
                                 hipStream_t stream, q8_path path) {
-    if (!valid_shape(N, K) || n_live < 1 || n_live > Q8_MAX_SLOTS || !aligned(Wq, 16) ||
-        !aligned(Xq, 16) || !aligned(batch_index, 4) || !aligned(Y, 4))
-        return Q8_ERR_INVALID_ARG;
+    if (!q8::matmul_args_ok(Wq, Xq, batch_index, n_live, N, K, Y)) return Q8_ERR_INVALID_ARG;
     if (path != Q8_PATH_AUTO && path != Q8_PATH_MFMA && path != Q8_PATH_DOT4)
         return Q8_ERR_INVALID_ARG;
     if (!current_device_ok()) return Q8_ERR_UNSUPPORTED;
@@ -155,9 +163,7 @@ q8_status q8_matmul_narrow_ws(const void* Wq, const void* Xq,
                               const int32_t* batch_index, int n_live, int64_t N,
                               int64_t K, float* Y, void* workspace,
                               size_t workspace_size, hipStream_t stream) {
-    if (!valid_shape(N, K) || n_live < 1 || n_live > Q8_MAX_SLOTS || !aligned(Wq, 16) ||
-        !aligned(Xq, 16) || !aligned(batch_index, 4) || !aligned(Y, 4))
-        return Q8_ERR_INVALID_ARG;
+    if (!q8::matmul_args_ok(Wq, Xq, batch_index, n_live, N, K, Y)) return Q8_ERR_INVALID_ARG;
     const q8::Shape s = q8::make_shape(N, K);
     const q8::Tiling t = q8::choose_tiling(s);
     const size_t need = q8::workspace_bytes(s, t);
@@ -235,6 +241,7 @@ const char* q8_status_str(q8_status status) {
         case Q8_ERR_INVALID_ARG: return "Q8_ERR_INVALID_ARG";
         case Q8_ERR_UNSUPPORTED: return "Q8_ERR_UNSUPPORTED";
         case Q8_ERR_HIP: return "Q8_ERR_HIP";
+        case Q8_ERR_TOO_LARGE: return "Q8_ERR_TOO_LARGE";
     }
     return "Q8_ERR_UNKNOWN";
 }

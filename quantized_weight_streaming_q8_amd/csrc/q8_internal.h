@@ -179,6 +179,11 @@ size_t workspace_bytes(const Shape& s, const Tiling& t);
 // (16 pages of 4 KB), then workspace_bytes().
 constexpr size_t kFusedFlagBytes = 64 * 1024;
 
+// Host checks shared by the matmul entry points: a valid shape, 1 <= n_live
+// <= 16, and non-null, aligned pointers.
+bool matmul_args_ok(const void* Wq, const void* Xq, const int32_t* batch_index, int n_live,
+                    int64_t N, int64_t K, const float* Y);
+
 enum class Engine { kMfma, kDot4 };
 // workspace: nullptr for the single-workgroup evaluation of the tree, or a
 // zero-initialised buffer of workspace_bytes() for the split execution.

@@ -29,7 +29,7 @@ def test_header_declares_the_abi():
     names = header_functions()
     for core in ("q8_pack_weights", "q8_quantize_acts", "q8_matmul_narrow"):
         assert core in names
-    assert len(names) == 19, names
+    assert len(names) == 20, names
 
 
 def test_every_declared_symbol_is_exported(q8):
@@ -44,8 +44,10 @@ def test_constants_agree_with_header(q8):
     assert int(re.search(r"#define Q8_MAX_SLOTS (\d+)", text).group(1)) == q8.Q8_MAX_SLOTS == 16
     assert int(re.search(r"#define Q8_BLOCK (\d+)", text).group(1)) == q8.Q8_BLOCK == 32
     assert int(re.search(r"#define Q8_MAX_COLUMNS (\d+)", text).group(1)) == q8.Q8_MAX_COLUMNS == 64
+    assert int(re.search(r"#define Q8_NOALLOC_SCRATCH_BYTES \((\d+)u << 20\)", text).group(1)) << 20 \
+        == q8.Q8_NOALLOC_SCRATCH_BYTES
     for name in ("Q8_OK", "Q8_ERR_INVALID_ARG", "Q8_ERR_UNSUPPORTED", "Q8_ERR_HIP",
-                 "Q8_PATH_AUTO", "Q8_PATH_MFMA", "Q8_PATH_DOT4"):
+                 "Q8_ERR_TOO_LARGE", "Q8_PATH_AUTO", "Q8_PATH_MFMA", "Q8_PATH_DOT4"):
         val = int(re.search(name + r"\s*=\s*(\d+)", text).group(1))
         assert getattr(q8, name) == val, name
 
@@ -55,6 +57,7 @@ def test_status_strings(q8):
     assert q8.status_str(1) == "Q8_ERR_INVALID_ARG"
     assert q8.status_str(2) == "Q8_ERR_UNSUPPORTED"
     assert q8.status_str(3) == "Q8_ERR_HIP"
+    assert q8.status_str(4) == "Q8_ERR_TOO_LARGE"
     assert q8.status_str(99) == "Q8_ERR_UNKNOWN"
 
 
@@ -123,6 +126,26 @@ def _rc(fn, *args):
 ])
 def test_matmul_rejects_invalid_arguments(q8, args):
     assert q8.library().q8_matmul_narrow(*args) == q8.Q8_ERR_INVALID_ARG
+    assert q8.library().q8_matmul_narrow_noalloc(*args) == q8.Q8_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_shapes_beyond_its_array(q8):
+    """The no-allocation entry point's static array holds the split records
+    of up to 1927 row groups; a split shape needing more is refused before
+    any HIP call, one that fits is not refused for its size."""
+    lib = q8.library()
+    cap = q8.Q8_NOALLOC_SCRATCH_BYTES
+    rec = 256 + 4 * 1024
+    assert cap // rec == 1927
+    fits, over = 1927 * 16, 1928 * 16
+    assert q8.q8_matmul_workspace_bytes(fits, 17408) <= cap < q8.q8_matmul_workspace_bytes(over, 17408)
+    assert lib.q8_matmul_narrow_noalloc(P, P, P, 4, over, 17408, P, None) == q8.Q8_ERR_TOO_LARGE
+    assert lib.q8_matmul_narrow_noalloc(P, P, P, 4, 10 ** 6, 8192, P, None) == q8.Q8_ERR_TOO_LARGE
+    # shapes that fit (or are not split) get past the size check; with no
+    # gfx950 device the call then stops at the device check
+    if not q8.q8_device_supported():
+        for N, K in ((fits, 17408), (151936, 5120)):
+            assert lib.q8_matmul_narrow_noalloc(P, P, P, 4, N, K, P, None) == q8.Q8_ERR_UNSUPPORTED
 
 
 def test_matmul_path_rejects_unknown_engine(q8):
