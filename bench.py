@@ -6,9 +6,11 @@ matrices (QKV 5120->7168, O 5120->5120, gate+up 5120->34816, down
 17408->5120) the 16-slot activation buffer is pre-quantised and the narrow
 matmul runs for the live batch, gathered through a seeded random
 batch_index (workspace entry point: K splits of small-N matrices spread
-over separate workgroups).  Weights are packed once, outside the timed region, in enough
-copies (rotated step by step) to exceed 1 GiB, so no step finds its weights
-in the 256 MB last-level cache.
+over separate workgroups).  Weights are packed once, outside the timed region.
+Each matrix rotates, step by step, through enough packed copies to exceed
+1 GiB on its own (28 of QKV, 39 of O, 6 of gate+up, 12 of down), so neither
+a step nor a single matrix's timing finds its weights in the 256 MB
+last-level cache.
 
 Reported (one JSON line): the whole step's achieved GB/s from algorithmic
 bytes (packed weights 34 B per 32 weights, the live tokens' activation
@@ -42,7 +44,9 @@ if ROOT not in sys.path:
 import workloads as wl  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, vendor figure
-COLD_BYTES = 1 << 30    # rotate weight copies past 1 GiB
+COLD_BYTES = 1 << 30    # rotate each matrix's weight copies past 1 GiB
+MAX_COPIES = 256        # ... but no more copies than this (tiny matrices)
+SETTLE_S = 0.25         # untimed steps before the warmup, so clocks have settled
 STEP_REPEATS = 11       # windows for the step time's median and p90
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -73,8 +77,15 @@ def step_bytes(matrices, n_live: int) -> int:
 
 # ------------------------------------------------------------------- GPU
 
+def copies_for(nbytes: int) -> int:
+    """Packed copies of a matrix whose rotation covers COLD_BYTES (at least
+    2, at most MAX_COPIES)."""
+    return int(min(MAX_COPIES, max(2, -(-COLD_BYTES // nbytes))))
+
+
 class Layer:
-    """R packed copies of a workload's matrices, plus the activation buffers."""
+    """Packed copies of a workload's matrices (each matrix its own rotation
+    of at least 1 GiB), plus the activation buffers."""
 
     def __init__(self, key: str, fused: bool = False):
         import torch
@@ -82,9 +93,9 @@ class Layer:
         self.q8 = q8
         self.w = wl.WORKLOADS[key]
         self.mats = list(self.w.matrices)
-        one = sum(q8.q8_packed_weight_bytes(m.N, m.K) for m in self.mats)
-        self.copies = max(1, -(-COLD_BYTES // one))
-        self.packed = [[None] * len(self.mats) for _ in range(self.copies)]
+        sizes = [q8.q8_packed_weight_bytes(m.N, m.K) for m in self.mats]
+        self.copies = [copies_for(b) for b in sizes]
+        self.packed = []
         self.fused = fused
         self.X, self.Xq, self.Y, self.ws, self.fws = [], [], [], [], []
         for i, m in enumerate(self.mats):
@@ -92,8 +103,7 @@ class Layer:
             base = q8.empty_packed_weights(m.N, m.K)
             q8.q8_pack_weights(W, m.N, m.K, base)
             del W
-            for c in range(self.copies):
-                self.packed[c][i] = base if c == 0 else base.clone()
+            self.packed.append([base] + [base.clone() for _ in range(self.copies[i] - 1)])
             self.X.append(torch.from_numpy(
                 wl.activations(self.w.config, m.K, outliers=self.w.outliers)).cuda())
             self.Xq.append(q8.empty_act_slots(m.K))
@@ -101,115 +111,140 @@ class Layer:
             self.ws.append(q8.zeroed_workspace(m.N, m.K))
             self.fws.append(q8.zeroed_fused_workspace(m.N, m.K))
         torch.cuda.synchronize()
-        self.packed_bytes = one
+        self.packed_bytes = sum(sizes)
+        self.cold_bytes = sum(c * b for c, b in zip(self.copies, sizes))
+
+    def weights(self, i: int, step: int):
+        """Matrix i's packed copy for step `step` of the rotation."""
+        return self.packed[i][step % self.copies[i]]
+
+    def launches(self, i: int) -> int:
+        """Back-to-back launches of matrix i in one timed graph: every copy
+        of its rotation at least once."""
+        return max(64, self.copies[i])
 
     def batch_index(self, n_live: int):
         import torch
         bi = wl.batch_index(self.w.config, n_live, random=self.w.random_batch_index)
         return torch.from_numpy(bi).cuda()
 
-    def step(self, copy: int, bi, n_live: int, events=None) -> None:
-        """Enqueue one step: for every matrix, pre-quantise the 16 slots and
-        run the narrow matmul, either in one fused launch or as the two
-        separate calls; with `events`, bracket every matrix's launches with a
-        pair of events recorded on the launch stream."""
+    def step(self, s: int, bi, n_live: int, events=None) -> None:
+        """Enqueue step s: for every matrix, pre-quantise the 16 slots and
+        run the narrow matmul on that step's weight copy, either in one fused
+        launch or as the two separate calls; with `events`, bracket every
+        matrix's launches with a pair of events recorded on the launch
+        stream."""
         q8 = self.q8
         for i, m in enumerate(self.mats):
             if events is not None:
                 events[i][0].record()
             if self.fused:
-                q8.q8_matmul_narrow_fused(self.packed[copy][i], self.X[i], 16, self.Xq[i], bi,
+                q8.q8_matmul_narrow_fused(self.weights(i, s), self.X[i], 16, self.Xq[i], bi,
                                           n_live, m.N, m.K, self.Y[i], self.fws[i])
             else:
                 q8.q8_quantize_acts(self.X[i], 16, m.K, self.Xq[i])
-                q8.q8_matmul_narrow_ws(self.packed[copy][i], self.Xq[i], bi, n_live, m.N, m.K,
+                q8.q8_matmul_narrow_ws(self.weights(i, s), self.Xq[i], bi, n_live, m.N, m.K,
                                        self.Y[i], self.ws[i])
             if events is not None:
                 events[i][1].record()
 
+    def settle(self, n_live: int, seconds: float = SETTLE_S) -> None:
+        """Untimed steps for `seconds` of wall time (setup: lets the clocks
+        and the page tables of every weight copy settle before the warmup)."""
+        import torch
+        bi = self.batch_index(n_live)
+        t0 = time.perf_counter()
+        s = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                self.step(s, bi, n_live)
+                s += 1
+            torch.cuda.synchronize()
+
+
+def _event_pair():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
 
 def time_steps(layer: Layer, n_live: int, steps: int, warmup: int, with_events: bool):
-    """Run `warmup` untimed steps, then time exactly `steps` steps between two
-    device synchronisations.  Returns (ms per step, per-matrix kernel ms
-    lists)."""
+    """Run `warmup` untimed steps, then time exactly `steps` steps between a
+    pair of HIP events on the launch stream, with a device synchronisation
+    on both sides.  Returns (ms per step, per-matrix kernel ms lists)."""
     import torch
     bi = layer.batch_index(n_live)
     for s in range(warmup):
-        layer.step(s % layer.copies, bi, n_live)
+        layer.step(s, bi, n_live)
     torch.cuda.synchronize()
     ev = []
     if with_events:
-        ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-               for _ in layer.mats] for _ in range(steps)]
-    t0 = time.perf_counter()
+        ev = [[list(_event_pair()) for _ in layer.mats] for _ in range(steps)]
+    e0, e1 = _event_pair()
+    e0.record()
     for s in range(steps):
-        layer.step(s % layer.copies, bi, n_live, ev[s] if with_events else None)
+        layer.step(warmup + s, bi, n_live, ev[s] if with_events else None)
+    e1.record()
     torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
     kern = [[] for _ in layer.mats]
     if with_events:
         for s in range(steps):
             for i in range(len(layer.mats)):
                 kern[i].append(ev[s][i][0].elapsed_time(ev[s][i][1]))
-    return dt * 1e3 / steps, kern
+    return e0.elapsed_time(e1) / steps, kern
 
 
-def steps_per_graph(copies: int, steps: int, most: int = 40) -> int:
-    """Steps one captured graph holds: the largest multiple of the weight
-    copies that divides `steps` (so exactly `steps` steps are replayed) and
-    is at most `most`; 1 if there is none."""
-    best = 1
-    for n in range(copies, most + 1, copies):
-        if steps % n == 0:
-            best = n
-    return best
+def steps_per_graph(steps: int, most: int = 40) -> int:
+    """Steps one captured graph holds: the largest divisor of `steps` that
+    is at most `most` (so exactly `steps` steps are replayed)."""
+    return max(n for n in range(1, min(most, steps) + 1) if steps % n == 0)
 
 
 def capture_step_graph(layer: Layer, n_live: int, spg: int):
     """One HIP graph holding `spg` whole steps (each the four quantise +
-    matmul pairs, the weight copies in rotation), captured through torch's
-    graph API on the stream the library launches on.  With several steps per
-    graph, the host's cost of launching a graph is spread over them."""
+    matmul pairs, each matrix's weight copies in rotation), captured through
+    torch's graph API on the stream the library launches on.  With several
+    steps per graph, the host's cost of launching a graph is spread over
+    them."""
     import torch
     bi = layer.batch_index(n_live)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for c in range(layer.copies):
-            layer.step(c, bi, n_live)
+        for k in range(spg):
+            layer.step(k, bi, n_live)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for k in range(spg):
-            layer.step(k % layer.copies, bi, n_live)
+            layer.step(k, bi, n_live)
     torch.cuda.synchronize()
     return g, bi
 
 
 def time_graph_steps(layer: Layer, n_live: int, steps: int, warmup: int):
     """Step time with the steps replayed from captured graphs of several
-    steps each (exactly `steps` steps in all).  Returns (ms per step, True if
-    every output of the last replay is bit-identical to an eager step on the
-    same inputs, steps per graph)."""
+    steps each (exactly `steps` steps in all), between a pair of HIP events.
+    Returns (ms per step, True if every output of the last replay is
+    bit-identical to an eager step on the same inputs, steps per graph)."""
     import torch
-    spg = steps_per_graph(layer.copies, steps)
+    spg = steps_per_graph(steps)
     g, bi = capture_step_graph(layer, n_live, spg)
     for _ in range(max(1, warmup // spg)):
         g.replay()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    e0, e1 = _event_pair()
+    e0.record()
     for _ in range(steps // spg):
         g.replay()
+    e1.record()
     torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    last = (spg - 1) % layer.copies
     got = [y.clone() for y in layer.Y]
-    layer.step(last, bi, n_live)
+    layer.step(spg - 1, bi, n_live)
     torch.cuda.synchronize()
     same = all(torch.equal(a.view(torch.int32), b.view(torch.int32)) for a, b in zip(got, layer.Y))
     del g
-    return dt * 1e3 / steps, same, spg
+    return e0.elapsed_time(e1) / steps, same, spg
 
 
 def run_schedule(layer: Layer, steps: int, warmup: int) -> dict:
@@ -231,12 +266,12 @@ def run_schedule(layer: Layer, steps: int, warmup: int) -> dict:
         for s in range(steps):
             if events is not None:
                 events[s][0].record()
-            layer.step(s % layer.copies, bis[s], ns[s])
+            layer.step(s, bis[s], ns[s])
             if events is not None:
                 events[s][1].record()
 
     for s in range(min(warmup, steps)):
-        layer.step(s % layer.copies, bis[s], ns[s])
+        layer.step(s, bis[s], ns[s])
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -248,7 +283,7 @@ def run_schedule(layer: Layer, steps: int, warmup: int) -> dict:
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for s in range(layer.copies):
+        for s in range(min(steps, 40)):
             layer.step(s, bis[s], ns[s])
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
@@ -263,7 +298,7 @@ def run_schedule(layer: Layer, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     ms_graph = e0.elapsed_time(e1)
     got = [y.clone() for y in layer.Y]
-    layer.step((steps - 1) % layer.copies, bis[-1], ns[-1])
+    layer.step(steps - 1, bis[-1], ns[-1])
     torch.cuda.synchronize()
     same = all(torch.equal(a.view(torch.int32), b.view(torch.int32)) for a, b in zip(got, layer.Y))
     del g
@@ -291,7 +326,7 @@ def run_schedule(layer: Layer, steps: int, warmup: int) -> dict:
         "ms_total_eager": round(ms_eager, 4), "ms_total_graph": round(ms_graph, 4),
         "graph_bit_identical": same,
         "timing": "one hip graph of the whole schedule" if ms is ms_graph else "eager launches",
-        "weight_copies_rotated": layer.copies,
+        "weight_copies_rotated": dict(zip((m.name for m in layer.mats), layer.copies)),
         "by_n_live": by_n,
     }
 
@@ -363,7 +398,7 @@ def kernel_stats_us(layer: Layer, i: int, n_live: int, launches: int, replays: i
     q8, m = layer.q8, layer.mats[i]
     bi = layer.batch_index(n_live)
     r = graph_replay_us(lambda c: q8.q8_matmul_narrow_ws(
-        layer.packed[c % layer.copies][i], layer.Xq[i], bi, n_live, m.N, m.K,
+        layer.weights(i, c), layer.Xq[i], bi, n_live, m.N, m.K,
         layer.Y[i], layer.ws[i]), launches, replays)
     return {"mean": float(np.mean(r)), "median": float(np.median(r)),
             "p90": float(np.percentile(r, 90)), "replays": replays, "launches_each": launches}
@@ -376,7 +411,7 @@ def kernel_avg_us(layer: Layer, i: int, n_live: int, launches: int) -> float:
     q8, m = layer.q8, layer.mats[i]
     bi = layer.batch_index(n_live)
     return graph_avg_us(lambda c: q8.q8_matmul_narrow_ws(
-        layer.packed[c % layer.copies][i], layer.Xq[i], bi, n_live, m.N, m.K,
+        layer.weights(i, c), layer.Xq[i], bi, n_live, m.N, m.K,
         layer.Y[i], layer.ws[i]), launches)
 
 
@@ -385,7 +420,7 @@ def fused_avg_us(layer: Layer, i: int, n_live: int, launches: int) -> float:
     q8, m = layer.q8, layer.mats[i]
     bi = layer.batch_index(n_live)
     return graph_avg_us(lambda c: q8.q8_matmul_narrow_fused(
-        layer.packed[c % layer.copies][i], layer.X[i], 16, layer.Xq[i], bi, n_live, m.N, m.K,
+        layer.weights(i, c), layer.X[i], 16, layer.Xq[i], bi, n_live, m.N, m.K,
         layer.Y[i], layer.fws[i]), launches)
 
 
@@ -439,6 +474,18 @@ def copy_ceiling_gbs(nbytes: int = 1 << 30, reps: int = 20) -> float:
 
 # ------------------------------------------------------------ CPU oracle
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or '' if unknown."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(key: str, n_live: int, seconds: float = 10.0):
     """The oracle as it stands, on the host cores: full passes over the
     workload's matrices at this live batch, repeated until `seconds` of
@@ -467,6 +514,7 @@ def cpu_baseline(key: str, n_live: int, seconds: float = 10.0):
         "value": round(nbytes / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": orc.num_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"{passes} full pass(es) of the {key} step (all {len(data)} matrices, "
                    f"quantise + matmul) at n_live={n_live}, {dt:.1f} s wall"),
@@ -483,8 +531,8 @@ def cpu_detail(key: str, runs: int = 3) -> dict:
     orc = oracle.get()
     w = wl.WORKLOADS[key]
     all_threads = orc.num_threads()
-    out = {"workload": key, "threads_all": all_threads, "runs": runs, "matrices": {},
-           "quantize": {}}
+    out = {"workload": key, "threads_all": all_threads, "cpu_model": cpu_model(), "runs": runs,
+           "matrices": {}, "quantize": {}}
     for i, m in enumerate(w.matrices):
         qw, dw = orc.quantize_rows(wl.weights(w.config, i, m.N, m.K))
         X = wl.activations(w.config, m.K, outliers=w.outliers)
@@ -560,7 +608,7 @@ def measured_traffic(workload: str, matrix: str, n_live: int, fused: bool):
 
 # ------------------------------------------------- multi-token columns
 
-def multi_columns(layer: Layer, widths, launches: int) -> dict:
+def multi_columns(layer: Layer, widths) -> dict:
     """The multi-column matmul (q8_matmul_multi) on every matrix of the
     workload with n columns (n slots, all live, seeded random batch_index),
     e.g. n_seq sequences x (k+1) speculative tokens: kernel time per launch,
@@ -578,7 +626,7 @@ def multi_columns(layer: Layer, widths, launches: int) -> dict:
             q8.q8_quantize_acts_n(X, n, m.K, Xq, n)
             Y = torch.empty((n, m.N), dtype=torch.float32, device="cuda")
             us = graph_avg_us(lambda c: q8.q8_matmul_multi(
-                layer.packed[c % layer.copies][i], Xq, n, bi, n, m.N, m.K, Y), launches)
+                layer.weights(i, c), Xq, n, bi, n, m.N, m.K, Y), layer.launches(i))
             rec[m.name] = {"us": round(us, 2), "GBps": round(matmul_bytes(m.N, m.K, n) / us / 1e3, 1)}
             del X, Xq, Y
         tot = sum(r["us"] for r in rec.values())
@@ -620,7 +668,7 @@ def rope_after_qkv(layer: Layer, n_live: int, launches: int = 100):
 
 # ------------------------------------------------------- engine A/B
 
-def engine_ab(layer: Layer, n_values, launches: int) -> dict:
+def engine_ab(layer: Layer, n_values) -> dict:
     """Both int8 dot engines (MFMA tiles against all 16 slots; v_dot4 with
     one row per lane and the live tokens' blocks through scalar loads) on
     every matrix of the workload, plain entry point, per live batch: the
@@ -633,8 +681,8 @@ def engine_ab(layer: Layer, n_values, launches: int) -> dict:
             rec = {}
             for name, path in (("mfma", q8.Q8_PATH_MFMA), ("dot4", q8.Q8_PATH_DOT4)):
                 us = graph_avg_us(lambda c: q8.q8_matmul_narrow_path(
-                    layer.packed[c % layer.copies][i], layer.Xq[i], bi, n, m.N, m.K,
-                    layer.Y[i], path=path), launches)
+                    layer.weights(i, c), layer.Xq[i], bi, n, m.N, m.K,
+                    layer.Y[i], path=path), layer.launches(i))
                 rec[name] = {"us": round(us, 2),
                              "GBps": round(matmul_bytes(m.N, m.K, n) / us / 1e3, 1)}
             out[f"{m.name} n_live={n}"] = rec
@@ -657,40 +705,43 @@ CAL_BYTES = 256 << 20
 
 
 def pmc_probe(key: str, launches: int, n_live: int, fused: bool) -> None:
-    """The dominant kernel of the workload's step (the fused pre-quantise +
-    matmul, or the matmul alone), `launches` times over two weight copies,
-    then the calibration copy three times."""
+    """Every matrix of the workload's step in turn (the fused pre-quantise +
+    matmul, or the matmul alone), `launches` times each over two weight
+    copies, then the calibration copy three times."""
     import torch
     import quantized_weight_streaming_q8_amd as q8
     w = wl.WORKLOADS[key]
-    i = dominant_matrix(key)
-    m = w.matrices[i]
-    W = torch.from_numpy(wl.weights(w.config, i, m.N, m.K)).cuda()
-    packed = [q8.empty_packed_weights(m.N, m.K) for _ in range(2)]
-    for P in packed:
-        q8.q8_pack_weights(W, m.N, m.K, P)
-    del W
-    X = torch.from_numpy(wl.activations(w.config, m.K, outliers=w.outliers)).cuda()
-    Xq = q8.empty_act_slots(m.K)
-    q8.q8_quantize_acts(X, 16, m.K, Xq)
-    Y = torch.empty((16, m.N), dtype=torch.float32, device="cuda")
-    ws = q8.zeroed_workspace(m.N, m.K)
-    fws = q8.zeroed_fused_workspace(m.N, m.K)
     bi = torch.from_numpy(wl.batch_index(w.config, n_live, random=w.random_batch_index)).cuda()
-    for c in range(launches):
-        if fused:
-            q8.q8_matmul_narrow_fused(packed[c % 2], X, 16, Xq, bi, n_live, m.N, m.K, Y, fws)
-        else:
-            q8.q8_matmul_narrow_ws(packed[c % 2], Xq, bi, n_live, m.N, m.K, Y, ws)
-    torch.cuda.synchronize()
+    for i, m in enumerate(w.matrices):
+        W = torch.from_numpy(wl.weights(w.config, i, m.N, m.K)).cuda()
+        packed = [q8.empty_packed_weights(m.N, m.K) for _ in range(2)]
+        for P in packed:
+            q8.q8_pack_weights(W, m.N, m.K, P)
+        del W
+        X = torch.from_numpy(wl.activations(w.config, m.K, outliers=w.outliers)).cuda()
+        Xq = q8.empty_act_slots(m.K)
+        q8.q8_quantize_acts(X, 16, m.K, Xq)
+        Y = torch.empty((16, m.N), dtype=torch.float32, device="cuda")
+        ws = q8.zeroed_workspace(m.N, m.K)
+        fws = q8.zeroed_fused_workspace(m.N, m.K)
+        torch.cuda.synchronize()
+        for c in range(launches):
+            if fused:
+                q8.q8_matmul_narrow_fused(packed[c % 2], X, 16, Xq, bi, n_live, m.N, m.K, Y, fws)
+            else:
+                q8.q8_matmul_narrow_ws(packed[c % 2], Xq, bi, n_live, m.N, m.K, Y, ws)
+        torch.cuda.synchronize()
+        del packed, X, Xq, Y, ws, fws
+        torch.cuda.empty_cache()
+        print(f"pmc probe: {launches} {'fused' if fused else 'matmul'} launches of {m.name} "
+              f"at n_live={n_live}", flush=True)
     a = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1)
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(f"pmc probe: {launches} {'fused' if fused else 'matmul'} launches of {m.name} at "
-          f"n_live={n_live}, 3 copies of {CAL_BYTES} B", flush=True)
+    print(f"pmc probe: 3 copies of {CAL_BYTES} B", flush=True)
 
 
 def _counter_rows(path: str, counter: str):
@@ -700,34 +751,49 @@ def _counter_rows(path: str, counter: str):
 
 
 def pmc_summarize(fetch_csv: str, write_csv: str, key: str, n_live: int, fused: bool,
-                  out: str) -> dict:
-    """Per-launch HBM bytes of the workload's dominant kernel from the two
-    counter passes, each scaled by the calibration copy."""
-    res = {"kernel_source_hash": kernel_source_hash(), "workload": key,
-           "matrix": wl.WORKLOADS[key].matrices[dominant_matrix(key)].name,
-           "n_live": n_live, "fused": fused,
-           "calibration_copy_bytes": CAL_BYTES}
-    per = {}
+                  launches: int) -> dict:
+    """Per-launch HBM bytes of each matrix's kernel from the two counter
+    passes over `bench.py --pmc-probe LAUNCHES` (the matmul dispatches in
+    dispatch order are LAUNCHES per matrix, in the workload's order), each
+    counter scaled by what it reads on the calibration copy.  Writes one
+    summary per matrix under profiles/ and returns them."""
+    mats = wl.WORKLOADS[key].matrices
+    per_m = {m.name: {} for m in mats}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path, name)
-        mm = [float(r["Counter_Value"]) for r in rows if "mm_mfma_kernel" in r["Kernel_Name"]]
-        last_mm = max(int(r["Dispatch_Id"]) for r in rows if "mm_mfma_kernel" in r["Kernel_Name"])
+        mm = sorted(((int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in rows
+                     if "mm_mfma_kernel" in r["Kernel_Name"]))
+        if len(mm) != launches * len(mats):
+            raise SystemExit(f"{path}: {len(mm)} matmul dispatches for {name}, expected "
+                             f"{launches} x {len(mats)}")
+        last_mm = mm[-1][0]
         cal = [float(r["Counter_Value"]) for r in rows
                if "copyBuffer" in r["Kernel_Name"] and int(r["Dispatch_Id"]) > last_mm]
-        if not mm or not cal:
-            raise SystemExit(f"{path}: no matmul or calibration dispatches for {name}")
+        if not cal:
+            raise SystemExit(f"{path}: no calibration dispatches for {name}")
         scale = (CAL_BYTES / 1024.0) / float(np.median(cal))  # counters are in KiB
-        per[name] = {"matmul_KiB_per_dispatch_median": float(np.median(mm)),
-                     "calibration_KiB_median": float(np.median(cal)),
-                     "scale": scale,
-                     "bytes_per_launch": float(np.median(mm)) * 1024.0 * scale,
-                     "dispatches": len(mm)}
-    res["counters"] = per
-    res["traffic_bytes_per_launch"] = {
-        str(n_live): int(per["FETCH_SIZE"]["bytes_per_launch"] + per["WRITE_SIZE"]["bytes_per_launch"])}
-    with open(out, "w") as f:
-        json.dump(res, f, indent=1)
-    return res
+        for j, m in enumerate(mats):
+            vals = [v for _, v in mm[j * launches:(j + 1) * launches]]
+            per_m[m.name][name] = {"matmul_KiB_per_dispatch_median": float(np.median(vals)),
+                                   "calibration_KiB_median": float(np.median(cal)),
+                                   "scale": scale,
+                                   "bytes_per_launch": float(np.median(vals)) * 1024.0 * scale,
+                                   "dispatches": len(vals)}
+    out = {}
+    for m in mats:
+        per = per_m[m.name]
+        traffic = int(per["FETCH_SIZE"]["bytes_per_launch"] + per["WRITE_SIZE"]["bytes_per_launch"])
+        res = {"kernel_source_hash": kernel_source_hash(), "workload": key, "matrix": m.name,
+               "K": m.K, "N": m.N, "n_live": n_live, "fused": fused,
+               "calibration_copy_bytes": CAL_BYTES, "counters": per,
+               "algorithmic_bytes_per_launch": matmul_bytes(m.N, m.K, n_live)
+               + (quantize_bytes(m.K) if fused else 0),
+               "traffic_bytes_per_launch": {str(n_live): traffic}}
+        res["traffic_over_algorithmic"] = round(traffic / res["algorithmic_bytes_per_launch"], 4)
+        with open(pmc_summary_path(key, m.name, fused), "w") as f:
+            json.dump(res, f, indent=1)
+        out[m.name] = res
+    return out
 
 
 # ------------------------------------------------------------------ main
@@ -747,10 +813,13 @@ def main(argv=None) -> int:
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--pmc-probe", type=int, default=0, metavar="LAUNCHES",
-                    help="only launch the dominant matmul this many times and the "
+                    help="only launch each matrix's matmul this many times, then the "
                          "calibration copy (for rocprofv3 --pmc)")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the traffic summary from two counter_collection.csv files")
+                    help="write the per-matrix traffic summaries from two counter_collection.csv "
+                         "files of --pmc-probe runs")
+    ap.add_argument("--pmc-launches", type=int, default=20,
+                    help="the LAUNCHES of the --pmc-probe runs being summarised")
     ap.add_argument("--fused", action="store_true",
                     help="run the step through the fused pre-quantise + matmul entry point "
                          "(one launch per matrix; default: separate launches, faster here)")
@@ -767,11 +836,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.pmc_summarize:
-        path = pmc_summary_path(args.workload,
-                                wl.WORKLOADS[args.workload].matrices[dominant_matrix(args.workload)].name,
-                                args.fused)
         print(json.dumps(pmc_summarize(*args.pmc_summarize, args.workload, args.n_live, args.fused,
-                                       path), indent=1))
+                                       args.pmc_launches), indent=1))
         return 0
 
     if args.gpus != 1:
@@ -799,7 +865,7 @@ def main(argv=None) -> int:
     layer = Layer(args.workload, fused=args.fused)
     mats = layer.mats
     if args.engine_ab:
-        res = engine_ab(layer, (1, 2, 4, 8, 16), max(16, 2 * layer.copies))
+        res = engine_ab(layer, (1, 2, 4, 8, 16))
         text = json.dumps({"engine_ab": res, "workload": args.workload})
         print(text, flush=True)
         if args.out:
@@ -815,7 +881,8 @@ def main(argv=None) -> int:
                 f.write(text + "\n")
         return 0
     print(f"# {args.workload}: {len(mats)} matrices, {layer.packed_bytes / 1e6:.1f} MB packed, "
-          f"{layer.copies} copies rotated", file=sys.stderr, flush=True)
+          f"copies rotated {dict(zip((m.name for m in mats), layer.copies))} "
+          f"({layer.cold_bytes / 1e9:.2f} GB)", file=sys.stderr, flush=True)
 
     def step_time(n_live, steps, warmup):
         """(ms per step, eager ms, graph ms or None): the faster of eager
@@ -830,8 +897,11 @@ def main(argv=None) -> int:
         return best, ms_e, ms_g, spg
 
     # the step the library's fused entry point runs (one launch per matrix),
-    # and the same step as separate pre-quantise and matmul launches
+    # and the same step as separate pre-quantise and matmul launches; first
+    # (setup, untimed) a quarter second of steps so that the clocks and the
+    # weight copies' page tables have settled
     layer.fused = args.fused
+    layer.settle(args.n_live)
     ms, ms_eager, ms_graph, graph_spg = step_time(args.n_live, args.steps, args.warmup)
     layer.fused = not args.fused
     ms_other = step_time(args.n_live, args.steps, args.warmup)[0]
@@ -845,13 +915,12 @@ def main(argv=None) -> int:
           file=sys.stderr, flush=True)
 
     # each kernel alone: back-to-back launches between one pair of events
-    launches = max(64, 4 * layer.copies)
     per_matrix = {}
     kern_us, fused_us = [], []
     for i, m in enumerate(mats):
-        st = kernel_stats_us(layer, i, args.n_live, launches)
+        st = kernel_stats_us(layer, i, args.n_live, layer.launches(i))
         us = st["mean"]
-        fu = fused_avg_us(layer, i, args.n_live, launches)
+        fu = fused_avg_us(layer, i, args.n_live, layer.launches(i))
         kern_us.append(us)
         fused_us.append(fu)
         b = matmul_bytes(m.N, m.K, args.n_live)
@@ -863,6 +932,8 @@ def main(argv=None) -> int:
             "frac_peak": round(b / us / 1e3 / PEAK_HBM_GBS, 4),
             "quantize_us": round(quantize_avg_us(layer, i), 2),
             "fused_us": round(fu, 2), "fused_GBps": round(fb / fu / 1e3, 1),
+            "traffic": measured_traffic(args.workload, m.name, args.n_live, False),
+            "weight_copies_rotated": layer.copies[i],
         }
     mm_bytes = sum(matmul_bytes(m.N, m.K, args.n_live) for m in mats)
     print(f"# matmuls alone: {sum(kern_us):.1f} us, {mm_bytes / sum(kern_us) / 1e3:.0f} GB/s; "
@@ -889,7 +960,7 @@ def main(argv=None) -> int:
     if args.sweep_steps > 0:
         for n in range(1, 17):
             ms_n, ms_e, _, _ = step_time(n, args.sweep_steps, min(args.warmup, 20))
-            kn = [kernel_avg_us(layer, i, n, max(16, 2 * layer.copies)) for i in range(len(mats))]
+            kn = [kernel_avg_us(layer, i, n, layer.launches(i)) for i in range(len(mats))]
             sweep[n] = {"ms_per_step": round(ms_n, 4), "ms_per_step_eager": round(ms_e, 4),
                         "GBps": round(step_bytes(mats, n) / (ms_n * 1e-3) / 1e9, 1),
                         "kernel_us": round(sum(kn), 2),
@@ -906,7 +977,7 @@ def main(argv=None) -> int:
             rec["kernel_t_over_t1"] = round(rec["kernel_us"] / sweep[1]["kernel_us"], 4)
         ratio = sweep[16]["t_over_t1"]
 
-    multi = multi_columns(layer, (16, 32, 48, 64), max(16, 4 * layer.copies)) \
+    multi = multi_columns(layer, (16, 32, 48, 64)) \
         if args.multi else None
     rope = rope_after_qkv(layer, args.n_live)
     if rope:
@@ -934,7 +1005,8 @@ def main(argv=None) -> int:
         "ms_per_step": round(ms, 5),
         "ms_per_step_eager": round(ms_eager, 5),
         "timing": (f"hip graph replay, {graph_spg} steps per graph (checked bit-identical to eager)"
-                   if ms is not ms_eager else "eager launches on one stream") + "; the faster of the two",
+                   if ms is not ms_eager else "eager launches on one stream")
+        + "; the faster of the two, each between a pair of hip events on the launch stream",
         "ms_per_step_graph": round(ms_graph, 5) if ms_graph is not None else None,
         "step_launches": "fused pre-quantise + matmul, one launch per matrix" if args.fused
         else "separate pre-quantise and matmul launches",
@@ -952,7 +1024,8 @@ def main(argv=None) -> int:
             "n_live": args.n_live, "slots": 16,
             "batch_index": "seeded random prefix of a slot permutation"
             if layer.w.random_batch_index else "identity",
-            "weight_copies_rotated": layer.copies, "cold_bytes": layer.copies * layer.packed_bytes,
+            "weight_copies_rotated": dict(zip((m.name for m in layer.mats), layer.copies)),
+            "cold_bytes": layer.cold_bytes,
         },
         "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
         "step_bytes": nbytes,

@@ -211,6 +211,11 @@ q8_status q8_matmul_narrow_noalloc(const void* Wq, const void* Xq,
  * shape is invalid. */
 size_t q8_matmul_fused_workspace_bytes(int64_t N, int64_t K);
 
+/* Byte offset, in a fused workspace, of a uint32 that counts the matmul
+ * workgroups whose wait for the published slots ran out (see below).  The
+ * library only ever adds to it; it is zero after the caller's zero-fill. */
+#define Q8_FUSED_TIMEOUTS_OFFSET 256
+
 /* q8_quantize_acts(X, n_rows, K, Xq) followed by q8_matmul_narrow_ws(Wq, Xq,
  * batch_index, n_live, N, K, Y, workspace) in one launch, with the same
  * results: Xq receives the same bits as q8_quantize_acts would write and Y
@@ -223,6 +228,13 @@ size_t q8_matmul_fused_workspace_bytes(int64_t N, int64_t K);
  * publish the slots; the matmul workgroups stream their first weights while
  * they wait for them.
  *
+ * The wait is bounded.  Should it ever run out (it cannot in a normal call:
+ * the quantising workgroups are dispatched first and wait on nothing), the
+ * workgroup writes quiet NaN over every output row it owns and adds one to
+ * the uint32 at byte Q8_FUSED_TIMEOUTS_OFFSET of the workspace, and the
+ * kernel still finishes; the call itself returns Q8_OK, since nothing is
+ * known on the host without a synchronisation.
+ *
  * workspace: device memory, 256-byte aligned, at least
  * q8_matmul_fused_workspace_bytes(N, K) bytes, zero-filled before its first
  * use.  Every completed call leaves its counters and flags at zero again (as
@@ -234,6 +246,20 @@ q8_status q8_matmul_narrow_fused(const void* Wq, const float* X, int n_rows, voi
                                  const int32_t* batch_index, int n_live, int64_t N,
                                  int64_t K, float* Y, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+
+/* q8_matmul_narrow_fused with the bound of the wait given: each matmul
+ * workgroup polls for the published slots at most max_spins times (1 ..
+ * 2^30; q8_matmul_narrow_fused uses 2^22, each poll followed by a short
+ * sleep).  quantize = 0 launches no quantising workgroups at all, so the
+ * slots are neither written nor published and every wait runs out: a way to
+ * exercise the failure path from the host (every output NaN, the timeout
+ * word raised, the workspace rearmed for the next call).  quantize = 1 is
+ * q8_matmul_narrow_fused.  Other arguments and errors as there. */
+q8_status q8_matmul_narrow_fused_bounded(const void* Wq, const float* X, int n_rows, void* Xq,
+                                         const int32_t* batch_index, int n_live, int64_t N,
+                                         int64_t K, float* Y, void* workspace,
+                                         size_t workspace_bytes, int max_spins, int quantize,
+                                         hipStream_t stream);
 
 /* ------------------------------------------------- multi-token columns */
 

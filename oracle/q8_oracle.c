@@ -18,7 +18,9 @@
  *    computed and applied in IEEE fp32 (correctly rounded division), values
  *    q = round-half-away-from-zero(x/d) clamped to [-127,127], and d stored
  *    as IEEE binary16 rounded to nearest-even with subnormals kept.  An
- *    all-zero block stores d = +0 and q = 0 without dividing.
+ *    all-zero block stores d = +0 and q = 0 without dividing, and so does a
+ *    block whose scale underflows to zero; a block holding a NaN or an
+ *    infinity stores q = 0 and a NaN scale (quantize_block states the rules).
  *
  *  - The narrow matmul.  Same page, same section: every 32-weight block is
  *    dotted against every live token's activation block.  For live token t
@@ -39,6 +41,7 @@
  * OpenMP only splits independent output rows; each output is computed by one
  * thread in the order written below.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -145,19 +148,36 @@ void q8o_f16_to_f32_array(const uint16_t* h, int64_t n, float* out) {
 /* ------------------------------------------------------------------------ */
 
 /* Quantise one block of 32 values.  Returns the fp32 scale d (before it is
- * stored as binary16) so callers can check invariants against it. */
+ * stored as binary16) so callers can check invariants against it.
+ *
+ * Blocks the pages' format leaves undefined get one stated rule each (the
+ * GPU quantiser follows the same rules):
+ *   - a block holding a NaN or an infinity stores q = 0 and the binary16
+ *     quiet NaN 0x7E00 as its scale, so every output that uses the block is
+ *     NaN (the function returns NaN);
+ *   - a block whose scale a/127 rounds to zero (a == 0, or a below
+ *     63.5 * 2^-149, where the quotient underflows) is the zero block,
+ *     d = +0 and q = 0, with no division by zero;
+ *   - otherwise the rule above, subnormal scales included. */
 static float quantize_block(const float* x, int8_t* q, uint16_t* d16) {
     float a = 0.0f;
+    int finite = 1;
     for (int i = 0; i < Q8O_BLOCK; ++i) {
         const float v = fabsf(x[i]);
-        if (v > a) a = v;
+        if (!(v <= FLT_MAX)) finite = 0; /* NaN or infinity */
+        else if (v > a) a = v;
     }
-    if (a == 0.0f) {
+    if (!finite) {
+        for (int i = 0; i < Q8O_BLOCK; ++i) q[i] = 0;
+        *d16 = 0x7e00u;
+        return NAN;
+    }
+    const float d = a / 127.0f; /* IEEE fp32 division, rounded to nearest */
+    if (d == 0.0f) {
         for (int i = 0; i < Q8O_BLOCK; ++i) q[i] = 0;
         *d16 = 0;
         return 0.0f;
     }
-    const float d = a / 127.0f; /* IEEE fp32 division, rounded to nearest */
     for (int i = 0; i < Q8O_BLOCK; ++i) {
         float r = roundf(x[i] / d); /* half away from zero */
         if (r > 127.0f) r = 127.0f;
@@ -271,7 +291,6 @@ int q8o_block_dots(const int8_t* qw, int64_t N, int64_t K, const int8_t* qx,
     return 0;
 }
 
-/* Number of OpenMP threads a parallel region here would use. */
 /* ------------------------------------------------------------------------
  * Pos-vector rotary position embedding.  "Batched decode: co-decode N live
  * sessions in one GPU pass" (antirez/ds4 PR #530), commit "CUDA: add
@@ -315,6 +334,7 @@ int q8o_rope(const float* Y, int64_t n_rows, int64_t row_stride, const int32_t* 
     return 0;
 }
 
+/* Number of OpenMP threads a parallel region here would use. */
 int q8o_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -29,6 +29,7 @@ Q8_ERR_UNSUPPORTED = 2
 Q8_ERR_HIP = 3
 Q8_ERR_TOO_LARGE = 4
 Q8_NOALLOC_SCRATCH_BYTES = 8 << 20
+Q8_FUSED_TIMEOUTS_OFFSET = 256
 
 Q8_PATH_AUTO = 0
 Q8_PATH_MFMA = 1
@@ -51,6 +52,8 @@ _SIGNATURES = {
     "q8_matmul_fused_workspace_bytes": ([_i64, _i64], ctypes.c_size_t),
     "q8_matmul_narrow_fused": ([_vp, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _vp, _vp,
                                 ctypes.c_size_t, _vp], _i32),
+    "q8_matmul_narrow_fused_bounded": ([_vp, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _vp, _vp,
+                                        ctypes.c_size_t, _i32, _i32, _vp], _i32),
     "q8_act_buffer_bytes_n": ([_i64, _i32], ctypes.c_size_t),
     "q8_quantize_acts_n": ([_vp, _i32, _i64, _vp, _i32, _vp], _i32),
     "q8_matmul_multi": ([_vp, _vp, _i32, _vp, _i32, _i64, _i64, _vp, _vp], _i32),
@@ -89,19 +92,54 @@ def library() -> ctypes.CDLL:
 
 # ------------------------------------------------------------------ helpers
 
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+_I8 = (torch.int8,)
+_H16 = (torch.int16, torch.float16)  # binary16 bits
+_ANY = None
+
+
+def _arg(x, name: str, dtypes=_ANY, need_bytes: int = 0):
+    """First check of argument `name` for the C ABI: a tensor's dtype (when
+    the argument has one), that it holds at least `need_bytes` bytes (0: no
+    size check, e.g. when the shape itself is invalid and the library will
+    reject the call) and that it is contiguous.  An int is a raw device
+    address and None is NULL; both pass unchecked (the library's own host
+    checks still apply).  Returns (name, x) for _dev."""
+    if x is None or isinstance(x, int):
+        return name, x
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name}: cannot pass {type(x).__name__} as a device pointer")
+    if dtypes is not None and x.dtype not in dtypes:
+        want = " or ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise ValueError(f"{name}: expected {want}, got {str(x.dtype).replace('torch.', '')}")
+    have = x.numel() * x.element_size()
+    if have < need_bytes:
+        raise ValueError(f"{name}: holds {have} bytes, the call needs at least {need_bytes}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    return name, x
+
+
+def _dev(*checked):
+    """Second check, once every argument has passed _arg: each tensor lives
+    on the current device.  Returns the device addresses, in order."""
+    out = []
+    for name, x in checked:
+        if isinstance(x, torch.Tensor):
+            if not x.is_cuda:
+                raise ValueError(f"{name}: expected a device tensor, got one on {x.device}")
+            if x.device.index != torch.cuda.current_device():
+                raise ValueError(f"{name}: on {x.device}, but the current device is "
+                                 f"cuda:{torch.cuda.current_device()}")
+            x = x.data_ptr()
+        out.append(x)
+    return out
+
+
 def _ptr(x) -> int | None:
     """Device address of a tensor (or an int address, or None for NULL)."""
-    if x is None:
-        return None
-    if isinstance(x, int):
-        return x
-    if isinstance(x, torch.Tensor):
-        if not x.is_cuda:
-            raise ValueError("expected a device tensor")
-        if not x.is_contiguous():
-            raise ValueError("expected a contiguous tensor")
-        return x.data_ptr()
-    raise TypeError(f"cannot pass {type(x).__name__} as a device pointer")
+    return _dev(_arg(x, "argument"))[0]
 
 
 def _stream(stream) -> int | None:
@@ -121,6 +159,12 @@ def status_str(status: int) -> str:
     return _lib.q8_status_str(int(status)).decode()
 
 
+def _n(count: int, size: int) -> int:
+    """Bytes of `count` elements of `size` bytes (0 for a non-positive count,
+    which the library rejects itself)."""
+    return count * size if count > 0 else 0
+
+
 # ----------------------------------------------------------------- the ABI
 
 def q8_packed_weight_bytes(N: int, K: int) -> int:
@@ -132,36 +176,48 @@ def q8_act_buffer_bytes(K: int) -> int:
 
 
 def q8_pack_weights(W, N: int, K: int, Wq, stream=None) -> None:
-    _check(_lib.q8_pack_weights(_ptr(W), N, K, _ptr(Wq), _stream(stream)),
-           "q8_pack_weights")
+    w, wq = _dev(_arg(W, "W", _F32, _n(N * K, 4)),
+                 _arg(Wq, "Wq", _ANY, q8_packed_weight_bytes(N, K)))
+    _check(_lib.q8_pack_weights(w, N, K, wq, _stream(stream)), "q8_pack_weights")
 
 
 def q8_pack_weights_q(q, d16, N: int, K: int, Wq, stream=None) -> None:
-    _check(_lib.q8_pack_weights_q(_ptr(q), _ptr(d16), N, K, _ptr(Wq), _stream(stream)),
-           "q8_pack_weights_q")
+    qq, dd, wq = _dev(_arg(q, "q", _I8, _n(N * K, 1)),
+                      _arg(d16, "d16", _H16, _n(N * (K // Q8_BLOCK), 2)),
+                      _arg(Wq, "Wq", _ANY, q8_packed_weight_bytes(N, K)))
+    _check(_lib.q8_pack_weights_q(qq, dd, N, K, wq, _stream(stream)), "q8_pack_weights_q")
 
 
 def q8_unpack_weights(Wq, N: int, K: int, q, d16, stream=None) -> None:
-    _check(_lib.q8_unpack_weights(_ptr(Wq), N, K, _ptr(q), _ptr(d16), _stream(stream)),
-           "q8_unpack_weights")
+    wq, qq, dd = _dev(_arg(Wq, "Wq", _ANY, q8_packed_weight_bytes(N, K)),
+                      _arg(q, "q", _I8, _n(N * K, 1)),
+                      _arg(d16, "d16", _H16, _n(N * (K // Q8_BLOCK), 2)))
+    _check(_lib.q8_unpack_weights(wq, N, K, qq, dd, _stream(stream)), "q8_unpack_weights")
 
 
 def q8_quantize_acts(X, n_rows: int, K: int, Xq, stream=None) -> None:
-    _check(_lib.q8_quantize_acts(_ptr(X), n_rows, K, _ptr(Xq), _stream(stream)),
-           "q8_quantize_acts")
+    x, xq = _dev(_arg(X, "X", _F32, _n(n_rows * K, 4)),
+                 _arg(Xq, "Xq", _ANY, q8_act_buffer_bytes(K)))
+    _check(_lib.q8_quantize_acts(x, n_rows, K, xq, _stream(stream)), "q8_quantize_acts")
+
+
+def _mm_checked(Wq, Xq, batch_index, n_live: int, N: int, K: int, Y, xq_bytes: int | None = None):
+    return [_arg(Wq, "Wq", _ANY, q8_packed_weight_bytes(N, K)),
+            _arg(Xq, "Xq", _ANY, q8_act_buffer_bytes(K) if xq_bytes is None else xq_bytes),
+            _arg(batch_index, "batch_index", _I32, _n(n_live, 4)),
+            _arg(Y, "Y", _F32, _n(n_live * N, 4))]
 
 
 def q8_matmul_narrow(Wq, Xq, batch_index, n_live: int, N: int, K: int, Y,
                      stream=None) -> None:
-    _check(_lib.q8_matmul_narrow(_ptr(Wq), _ptr(Xq), _ptr(batch_index), n_live,
-                                 N, K, _ptr(Y), _stream(stream)),
-           "q8_matmul_narrow")
+    wq, xq, bi, y = _dev(*_mm_checked(Wq, Xq, batch_index, n_live, N, K, Y))
+    _check(_lib.q8_matmul_narrow(wq, xq, bi, n_live, N, K, y, _stream(stream)), "q8_matmul_narrow")
 
 
 def q8_matmul_narrow_path(Wq, Xq, batch_index, n_live: int, N: int, K: int, Y,
                           path: int, stream=None) -> None:
-    _check(_lib.q8_matmul_narrow_path(_ptr(Wq), _ptr(Xq), _ptr(batch_index), n_live,
-                                      N, K, _ptr(Y), _stream(stream), int(path)),
+    wq, xq, bi, y = _dev(*_mm_checked(Wq, Xq, batch_index, n_live, N, K, Y))
+    _check(_lib.q8_matmul_narrow_path(wq, xq, bi, n_live, N, K, y, _stream(stream), int(path)),
            "q8_matmul_narrow_path")
 
 
@@ -169,20 +225,28 @@ def q8_matmul_workspace_bytes(N: int, K: int) -> int:
     return int(_lib.q8_matmul_workspace_bytes(N, K))
 
 
+def _ws_bytes(workspace, workspace_bytes):
+    if workspace_bytes is not None:
+        return workspace_bytes
+    if isinstance(workspace, torch.Tensor):
+        return workspace.numel() * workspace.element_size()
+    return 0
+
+
 def q8_matmul_narrow_ws(Wq, Xq, batch_index, n_live: int, N: int, K: int, Y,
                         workspace, workspace_bytes: int | None = None,
                         stream=None) -> None:
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(_lib.q8_matmul_narrow_ws(_ptr(Wq), _ptr(Xq), _ptr(batch_index), n_live, N, K,
-                                    _ptr(Y), _ptr(workspace), workspace_bytes, _stream(stream)),
+    wq, xq, bi, y, ws = _dev(*_mm_checked(Wq, Xq, batch_index, n_live, N, K, Y),
+                             _arg(workspace, "workspace", _ANY, q8_matmul_workspace_bytes(N, K)))
+    _check(_lib.q8_matmul_narrow_ws(wq, xq, bi, n_live, N, K, y, ws,
+                                    _ws_bytes(workspace, workspace_bytes), _stream(stream)),
            "q8_matmul_narrow_ws")
 
 
 def q8_matmul_narrow_noalloc(Wq, Xq, batch_index, n_live: int, N: int, K: int, Y,
                              stream=None) -> None:
-    _check(_lib.q8_matmul_narrow_noalloc(_ptr(Wq), _ptr(Xq), _ptr(batch_index), n_live, N, K,
-                                         _ptr(Y), _stream(stream)),
+    wq, xq, bi, y = _dev(*_mm_checked(Wq, Xq, batch_index, n_live, N, K, Y))
+    _check(_lib.q8_matmul_narrow_noalloc(wq, xq, bi, n_live, N, K, y, _stream(stream)),
            "q8_matmul_narrow_noalloc")
 
 
@@ -190,14 +254,36 @@ def q8_matmul_fused_workspace_bytes(N: int, K: int) -> int:
     return int(_lib.q8_matmul_fused_workspace_bytes(N, K))
 
 
+def _fused_ptrs(Wq, X, n_rows, Xq, batch_index, n_live, N, K, Y, workspace):
+    mm = _mm_checked(Wq, Xq, batch_index, n_live, N, K, Y)
+    return _dev(mm[0], _arg(X, "X", _F32, _n(n_rows * K, 4)), mm[1], mm[2], mm[3],
+                _arg(workspace, "workspace", _ANY, q8_matmul_fused_workspace_bytes(N, K)))
+
+
 def q8_matmul_narrow_fused(Wq, X, n_rows: int, Xq, batch_index, n_live: int, N: int, K: int,
                            Y, workspace, workspace_bytes: int | None = None,
                            stream=None) -> None:
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(_lib.q8_matmul_narrow_fused(_ptr(Wq), _ptr(X), n_rows, _ptr(Xq), _ptr(batch_index),
-                                       n_live, N, K, _ptr(Y), _ptr(workspace), workspace_bytes,
-                                       _stream(stream)), "q8_matmul_narrow_fused")
+    wq, x, xq, bi, y, ws = _fused_ptrs(Wq, X, n_rows, Xq, batch_index, n_live, N, K, Y, workspace)
+    _check(_lib.q8_matmul_narrow_fused(wq, x, n_rows, xq, bi, n_live, N, K, y, ws,
+                                       _ws_bytes(workspace, workspace_bytes), _stream(stream)),
+           "q8_matmul_narrow_fused")
+
+
+def q8_matmul_narrow_fused_bounded(Wq, X, n_rows: int, Xq, batch_index, n_live: int, N: int,
+                                   K: int, Y, workspace, max_spins: int, quantize: int,
+                                   workspace_bytes: int | None = None, stream=None) -> None:
+    wq, x, xq, bi, y, ws = _fused_ptrs(Wq, X, n_rows, Xq, batch_index, n_live, N, K, Y, workspace)
+    _check(_lib.q8_matmul_narrow_fused_bounded(wq, x, n_rows, xq, bi, n_live, N, K, y, ws,
+                                               _ws_bytes(workspace, workspace_bytes),
+                                               int(max_spins), int(quantize), _stream(stream)),
+           "q8_matmul_narrow_fused_bounded")
+
+
+def fused_timeouts(workspace) -> int:
+    """The fused workspace's count of matmul workgroups whose wait ran out
+    (reads 4 bytes back from the device; synchronises)."""
+    w = workspace[Q8_FUSED_TIMEOUTS_OFFSET:Q8_FUSED_TIMEOUTS_OFFSET + 4]
+    return int.from_bytes(bytes(w.cpu().numpy().tobytes()), "little")
 
 
 def q8_act_buffer_bytes_n(K: int, n_slots: int) -> int:
@@ -205,24 +291,31 @@ def q8_act_buffer_bytes_n(K: int, n_slots: int) -> int:
 
 
 def q8_quantize_acts_n(X, n_rows: int, K: int, Xq, n_slots: int, stream=None) -> None:
-    _check(_lib.q8_quantize_acts_n(_ptr(X), n_rows, K, _ptr(Xq), n_slots, _stream(stream)),
+    x, xq = _dev(_arg(X, "X", _F32, _n(n_rows * K, 4)),
+                 _arg(Xq, "Xq", _ANY, q8_act_buffer_bytes_n(K, n_slots)))
+    _check(_lib.q8_quantize_acts_n(x, n_rows, K, xq, n_slots, _stream(stream)),
            "q8_quantize_acts_n")
 
 
 def q8_matmul_multi(Wq, Xq, n_slots: int, batch_index, n_live: int, N: int, K: int, Y,
                     stream=None) -> None:
-    _check(_lib.q8_matmul_multi(_ptr(Wq), _ptr(Xq), n_slots, _ptr(batch_index), n_live, N, K,
-                                _ptr(Y), _stream(stream)), "q8_matmul_multi")
+    wq, xq, bi, y = _dev(*_mm_checked(Wq, Xq, batch_index, n_live, N, K, Y,
+                                      xq_bytes=q8_act_buffer_bytes_n(K, n_slots)))
+    _check(_lib.q8_matmul_multi(wq, xq, n_slots, bi, n_live, N, K, y, _stream(stream)),
+           "q8_matmul_multi")
 
 
 def q8_rope_multi(Y, n_rows: int, row_stride: int, pos, n_heads: int, head_dim: int,
                   base: float, stream=None) -> None:
-    _check(_lib.q8_rope_multi(_ptr(Y), n_rows, row_stride, _ptr(pos), n_heads, head_dim,
-                              float(base), _stream(stream)), "q8_rope_multi")
+    need = _n((n_rows - 1) * row_stride + n_heads * head_dim, 4) if n_rows > 0 else 0
+    y, p = _dev(_arg(Y, "Y", _F32, need), _arg(pos, "pos", _I32, _n(n_rows, 4)))
+    _check(_lib.q8_rope_multi(y, n_rows, row_stride, p, n_heads, head_dim, float(base),
+                              _stream(stream)), "q8_rope_multi")
 
 
 def q8_stream_read(buf, nbytes: int, sink, stream=None) -> None:
-    _check(_lib.q8_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "q8_stream_read")
+    b, sk = _dev(_arg(buf, "buf", _ANY, max(nbytes, 0)), _arg(sink, "sink", _I32, 4 * 1024))
+    _check(_lib.q8_stream_read(b, nbytes, sk, _stream(stream)), "q8_stream_read")
 
 
 def q8_device_supported() -> bool:

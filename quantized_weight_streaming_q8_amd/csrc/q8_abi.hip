@@ -181,13 +181,15 @@ size_t q8_matmul_fused_workspace_bytes(int64_t N, int64_t K) {
     return q8::kFusedFlagBytes + q8::workspace_bytes(s, q8::choose_tiling(s));
 }
 
-q8_status q8_matmul_narrow_fused(const void* Wq, const float* X, int n_rows, void* Xq,
-                                 const int32_t* batch_index, int n_live, int64_t N,
-                                 int64_t K, float* Y, void* workspace,
-                                 size_t workspace_size, hipStream_t stream) {
+q8_status q8_matmul_narrow_fused_bounded(const void* Wq, const float* X, int n_rows, void* Xq,
+                                         const int32_t* batch_index, int n_live, int64_t N,
+                                         int64_t K, float* Y, void* workspace,
+                                         size_t workspace_size, int max_spins, int quantize,
+                                         hipStream_t stream) {
     if (!valid_shape(N, K) || n_rows < 1 || n_rows > Q8_MAX_SLOTS || n_live < 1 ||
         n_live > Q8_MAX_SLOTS || !aligned(Wq, 16) || !aligned(X, 16) || !aligned(Xq, 16) ||
-        !aligned(batch_index, 4) || !aligned(Y, 4))
+        !aligned(batch_index, 4) || !aligned(Y, 4) || max_spins < 1 || max_spins > (1 << 30) ||
+        (quantize != 0 && quantize != 1))
         return Q8_ERR_INVALID_ARG;
     const size_t need = q8_matmul_fused_workspace_bytes(N, K);
     if (!aligned(workspace, 256) || workspace_size < need) return Q8_ERR_INVALID_ARG;
@@ -195,7 +197,17 @@ q8_status q8_matmul_narrow_fused(const void* Wq, const float* X, int n_rows, voi
     const q8::Shape s = q8::make_shape(N, K);
     return from_hip(q8::launch_matmul_fused(static_cast<const uint8_t*>(Wq), X, n_rows,
                                             static_cast<uint8_t*>(Xq), batch_index, n_live, s,
-                                            q8::choose_tiling(s), Y, workspace, stream));
+                                            q8::choose_tiling(s), Y, workspace, max_spins,
+                                            quantize != 0, stream));
+}
+
+q8_status q8_matmul_narrow_fused(const void* Wq, const float* X, int n_rows, void* Xq,
+                                 const int32_t* batch_index, int n_live, int64_t N,
+                                 int64_t K, float* Y, void* workspace,
+                                 size_t workspace_size, hipStream_t stream) {
+    return q8_matmul_narrow_fused_bounded(Wq, X, n_rows, Xq, batch_index, n_live, N, K, Y,
+                                          workspace, workspace_size, q8::kFusedMaxSpins, 1,
+                                          stream);
 }
 
 q8_status q8_matmul_multi(const void* Wq, const void* Xq, int n_slots,

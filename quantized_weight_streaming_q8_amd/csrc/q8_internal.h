@@ -108,28 +108,45 @@ __device__ inline int64_t packed_d_index(int64_t row, int64_t blk, int64_t NSC) 
 // together hold a 32-value block: lanes l, l ^ L, l ^ 2L and l ^ 3L (L = 1:
 // 4 consecutive lanes starting at a multiple of 4; L = 16: lanes 16 apart).
 // All of them must be active.
+//
+// Blocks the format leaves undefined follow one stated rule each: a block
+// holding a NaN or an infinity stores q = 0 and the binary16 quiet NaN
+// 0x7E00 (every output that uses it is then NaN); a block whose scale
+// absmax/127 rounds to zero (absmax 0, or so small the quotient underflows)
+// is the zero block, q = 0 and d = +0.
 // ------------------------------------------------------------------------
 struct QuantSeg {
     uint32_t lo, hi;  // 8 int8 values, little-endian
     uint16_t d16;     // binary16 scale of the block
 };
 
+constexpr uint16_t kNanScale = 0x7E00;  // binary16 quiet NaN
+
 template <int L = 1>
 __device__ inline QuantSeg quantize_segment(const float v[8]) {
     static_assert(L == 1 || L == 16, "lane distance of a block's segments");
+    // absmax, with a NaN or an infinity counted as +infinity (fmaxf alone
+    // would drop a NaN)
     float a = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+    for (int i = 0; i < 8; ++i) {
+        const float m = fabsf(v[i]);
+        a = fmaxf(a, m <= __FLT_MAX__ ? m : __builtin_inff());
+    }
     // absmax of the 32-value block across the 4-lane group (max is exact)
     a = fmaxf(a, __shfl_xor(a, L, 4 * L));
     a = fmaxf(a, __shfl_xor(a, 2 * L, 4 * L));
     QuantSeg r;
-    if (a == 0.0f) {
-        r.lo = r.hi = 0u;
-        r.d16 = 0;
+    r.lo = r.hi = 0u;
+    if (!(a <= __FLT_MAX__)) {  // a NaN or an infinity in the block
+        r.d16 = kNanScale;
         return r;
     }
     const float d = a / 127.0f;  // correctly rounded (no fast-math)
+    if (d == 0.0f) {             // the zero block, or a scale that underflows
+        r.d16 = 0;
+        return r;
+    }
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -176,8 +193,13 @@ hipError_t launch_rope_multi(float* Y, int n_rows, int64_t row_stride, const int
 // Workspace a split execution needs (0: the shape is not split).
 size_t workspace_bytes(const Shape& s, const Tiling& t);
 // Workspace of the fused pre-quantise + matmul: 64 KB of counters and flags
-// (16 pages of 4 KB), then workspace_bytes().
+// (16 pages of 4 KB), then workspace_bytes().  The uint32 at byte
+// kFusedTimeoutsOffset counts the matmul workgroups whose bounded wait ran
+// out; the library never clears it.
 constexpr size_t kFusedFlagBytes = 64 * 1024;
+constexpr size_t kFusedTimeoutsOffset = 256;
+// Polls of the fused path's bounded wait (each followed by a short sleep).
+constexpr int kFusedMaxSpins = 1 << 22;
 
 // Host checks shared by the matmul entry points: a valid shape, 1 <= n_live
 // <= 16, and non-null, aligned pointers.
@@ -196,10 +218,13 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
 // Pre-quantise X [n_rows][K] into the 16-slot buffer Xq and run the matmul,
 // in one launch (MFMA engine).  workspace: kFusedFlagBytes of counters
 // followed by workspace_bytes() for the split execution, all zero before
-// the first call and left zero by every call.
+// the first call and left zero by every call (but the timeout word).
+// max_spins bounds each matmul workgroup's wait for the slots; quantize =
+// false launches no producers at all (the wait can then only run out).
 hipError_t launch_matmul_fused(const uint8_t* Wq, const float* X, int n_rows,
                                uint8_t* Xq, const int32_t* batch_index, int n_live,
                                const Shape& s, const Tiling& t, float* Y,
-                               void* workspace, hipStream_t st);
+                               void* workspace, int max_spins, bool quantize,
+                               hipStream_t st);
 
 }  // namespace q8

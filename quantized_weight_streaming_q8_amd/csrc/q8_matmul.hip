@@ -54,9 +54,6 @@
 
 #include <algorithm>
 #include <type_traits>
-#ifdef Q8_TUNING
-#include <cstdlib>
-#endif
 
 namespace q8 {
 namespace {
@@ -116,6 +113,7 @@ struct MmArgs {
     int S, KW;            // summation tree: splits, wave slices per split
     int n_rb;             // row blocks (RG row groups each)
     int CT;               // slot column tiles (16 slots each)
+    int y_vec4;           // N % 4 == 0 and Y 16-byte aligned: rows stored as float4
     int64_t xq_gs;        // slot buffer: bytes per 16 slots of the q region
     int64_t xd_gs;        // slot buffer: halves per 16 slots of the scale region
     // fused pre-quantisation (FUSED kernels only)
@@ -123,11 +121,13 @@ struct MmArgs {
     int n_rows;
     int P;                // producer workgroups, blockIdx.x < P
     int n_cons;           // consumer (matmul) workgroups
+    int max_spins;        // polls of the bounded wait
     uint32_t* qflag;      // producer groups that have published their slots
-    uint32_t* qdone;      // consumer groups past the wait
+    uint32_t* qexit;      // workgroups (producers and consumers) that are done
     uint32_t* qflag_sub;  // kSubCounters producer counters, kSubStride apart
-    uint32_t* qdone_sub;  // kSubCounters consumer counters, kSubStride apart
+    uint32_t* qexit_sub;  // kSubCounters exit counters, kSubStride apart
     uint32_t* qready;     // kReadyCopies "slots published" flags, kReadyStride apart
+    uint32_t* timeouts;   // matmul workgroups whose wait ran out (never cleared here)
 };
 
 // Super-chunk range [lo, hi) of wave slice k of split s (NSC <= 2^16, so 32-bit
@@ -377,35 +377,6 @@ __device__ inline void coherent_store(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Output element o of a tile, numbered token-major so that 16 consecutive
-// threads store 16 consecutive rows of one token (64 contiguous bytes):
-// o = (t*RG + rg)*16 + j is token t, row (gbase + rg)*16 + j.  The waves
-// wrote row j = 4*tq + r of slot s = 16*ct + l at tile element
-// ((rg*CT + ct)*4 + r)*64 + tq*16 + l.
-struct TileOut {
-    int t;        // token
-    int e;        // tile element of the token's slot column
-    int64_t n;    // output row
-    bool store;   // inside the matrix, a live token, a row group of this block
-    bool bad;     // the token's slot index is outside [0, 16*CT)
-};
-
-template <int RG, int CT>
-__device__ inline TileOut tile_out(const MmArgs& a, const int* tok_slot, int o,
-                                   int64_t gbase, int gskip) {
-    TileOut r;
-    r.t = o / (RG * 16);
-    const int rg = (o >> 4) & (RG - 1);
-    const int j = o & 15;
-    r.n = (gbase + rg) * kRowsPerGroup + j;
-    r.store = rg >= gskip && r.t < a.n_live && r.n < a.N;
-    const int s = tok_slot[r.t];
-    r.bad = s < 0 || s >= 16 * CT;
-    const int ss = r.bad ? 0 : s;
-    r.e = ((rg * CT + (ss >> 4)) * 4 + (j & 3)) * 64 + (j >> 2) * 16 + (ss & 15);
-    return r;
-}
-
 // ------------------------------------------------------------------------
 // Fused pre-quantisation.  The first P workgroups of a FUSED launch quantise
 // X into the slot buffer (the q8_0 rule of the separate pre-quantiser, same
@@ -413,15 +384,31 @@ __device__ inline TileOut tile_out(const MmArgs& a, const int* tok_slot, int o,
 // complete and arrive at the producer counter (two levels, see arrive_last);
 // the last of them raises the "published" flags.
 // The matmul workgroups put their first weight chunks in flight, then wait
-// for their flag before their first activation load.  Workgroups are dispatched in index order, so the producers are
-// resident or done before any matmul workgroup waits, and they wait on
-// nothing themselves.  The wait is bounded all the same (kMaxSpins polls):
-// were it ever to run out, the outputs would be wrong (and tests would say
-// so) but the kernel would still finish.  The last matmul workgroup past the
-// wait rearms all the counters for the next call.
+// for their flag before their first activation load.  Workgroups are
+// dispatched in index order, so the producers are resident or done before
+// any matmul workgroup waits, and they wait on nothing themselves.  The wait
+// is bounded all the same (max_spins polls): a workgroup whose wait runs out
+// writes quiet NaN over all its outputs (a split publishes a NaN partial, so
+// the combined rows are NaN too) and counts itself in the workspace's
+// timeout word, which the library never clears, so the failure is loud.
+// Every workgroup, producer or matmul, finally arrives at an exit counter
+// (after waiting for its own stores and atomics to complete); the last of
+// all P + n_cons arrivals rearms the counters and flags.  Nothing can touch
+// them after that: every producer has raised what it raises and every
+// matmul workgroup has stopped polling.
+//
+// Why the matmul workgroups may read the slots with plain loads after a
+// relaxed poll: every dispatch begins with an agent-scope acquire that
+// invalidates the L2 of every XCD (the slot buffer lives in ordinary
+// coarse-grained memory), so no line of the slot buffer cached by an
+// earlier kernel survives into this one; within the launch no workgroup
+// loads a slot line before its flag reads 1 (the loads are issued after the
+// poll, behind a workgroup barrier, and are not speculated), and the flag is
+// raised only after every producer's device-coherent stores have completed.
+// Every slot line that enters any cache during the launch therefore holds
+// the published bytes.
 // ------------------------------------------------------------------------
 
-constexpr int kMaxSpins = 1 << 22;
 // The "published" signal is polled by one thread per workgroup, each on one
 // of kReadyCopies flags that sit in different memory pages (4 KB apart), so
 // that the polls of a large grid do not all queue on one memory channel.
@@ -444,6 +431,29 @@ __device__ inline bool arrive_last(uint32_t* top, uint32_t* sub, int id, int n) 
         return false;
     return __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
            (uint32_t)(groups - 1);
+}
+
+// Wait until this thread's earlier memory operations (stores and atomics)
+// have completed.
+__device__ inline void wait_memory() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Called by thread 0 of every workgroup of a FUSED launch, last thing: the
+// last of all arrivals rearms every counter and flag for the next call.
+__device__ inline void fused_exit(const MmArgs& a) {
+    wait_memory();
+    if (!arrive_last(a.qexit, a.qexit_sub, (int)blockIdx.x, a.P + a.n_cons)) return;
+    __hip_atomic_store(a.qflag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.qexit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int k = 0; k < kSubCounters; ++k) {
+        __hip_atomic_store(a.qflag_sub + k * kSubStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.qexit_sub + k * kSubStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (int k = 0; k < kReadyCopies; ++k)
+        __hip_atomic_store(a.qready + k * kReadyStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ void produce_slots(const MmArgs& a, int pid) {
@@ -478,34 +488,139 @@ __device__ void produce_slots(const MmArgs& a, int pid) {
                                (uint32_t)r.d16 | (d_next << 16), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    wait_memory();
     __syncthreads();
-    if (threadIdx.x == 0 && arrive_last(a.qflag, a.qflag_sub, pid, a.P)) {
-        // the last producer: every slot is published; raise all the flags
-        for (int k = 0; k < kReadyCopies; ++k)
-            __hip_atomic_store(a.qready + k * kReadyStride, 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+        if (arrive_last(a.qflag, a.qflag_sub, pid, a.P)) {
+            // the last producer: every slot is published; raise all the flags
+            for (int k = 0; k < kReadyCopies; ++k)
+                __hip_atomic_store(a.qready + k * kReadyStride, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        fused_exit(a);
     }
 }
 
 // Called by every thread of a matmul workgroup: thread 0 polls the
-// workgroup's flag, the others wait at the barriers.
-__device__ inline void wait_for_slots(const MmArgs& a, int bid) {
+// workgroup's flag, at most a.max_spins times, the others wait at the
+// barriers.  Returns true (in every thread) if the wait ran out; thread 0
+// has then counted the workgroup in the timeout word.
+__device__ inline bool wait_for_slots(const MmArgs& a, int bid, int* shared_flag) {
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t* f = a.qready + (bid % kReadyCopies) * kReadyStride;
-        for (int spins = 0; spins < kMaxSpins; ++spins) {
-            if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+        int ready = 0;
+        for (int spins = 0; spins < a.max_spins; ++spins) {
+            if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+                ready = 1;
+                break;
+            }
             __builtin_amdgcn_s_sleep(4);
         }
+        if (!ready)
+            __hip_atomic_fetch_add(a.timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *shared_flag = !ready;
     }
     __syncthreads();
+    return *shared_flag != 0;
+}
+
+// An output unit is 4 consecutive rows of one row group for one token: unit
+// v of the n_live x RG x 4 units of a tile is token v / (4 RG), row group
+// (v / 4) % RG, rows 4 (v % 4) .. +3.  Consecutive threads take consecutive
+// units, so four threads store a token's 16 rows of a row group (64
+// contiguous bytes).  Rows past N and row groups before gskip (owned by the
+// previous row block) are not stored.
+template <int RG>
+__device__ inline void store_unit(const MmArgs& a, int v, int64_t gbase, int gskip, float4 y) {
+    const int t = v / (4 * RG), rg = (v >> 2) & (RG - 1), q = v & 3;
+    if (rg < gskip) return;
+    const int64_t n0 = (gbase + rg) * kRowsPerGroup + 4 * q;
+    float* yrow = a.Y + (int64_t)t * a.N;
+    if (a.y_vec4 && n0 + 3 < a.N) {
+        *reinterpret_cast<float4*>(yrow + n0) = y;
+    } else {
+        if (n0 < a.N) yrow[n0] = y.x;
+        if (n0 + 1 < a.N) yrow[n0 + 1] = y.y;
+        if (n0 + 2 < a.N) yrow[n0 + 2] = y.z;
+        if (n0 + 3 < a.N) yrow[n0 + 3] = y.w;
+    }
+}
+
+__device__ inline float4 add4(float4 p, float4 q) {
+    return make_float4(p.x + q.x, p.y + q.y, p.z + q.z, p.w + q.w);
+}
+
+// The sums of this thread's units over the NW waves of the workgroup, in the
+// tree's order: waves in order within a split, splits (of KW waves each) in
+// order.  red4 holds the waves' partial tiles as [wave][rg][slot][4 rows]
+// float4s; col[i] is unit i's slot column.  NW is a template parameter so
+// that every LDS read of a unit is issued before any add, with no branch.
+template <int NW, int RG, int SL, int MU>
+__device__ inline void tile_sums(const float4* red4, const int col[MU], int nthreads, int S,
+                                 int KW, float4 y[MU]) {
+#pragma unroll
+    for (int i = 0; i < MU; ++i) {
+        const int v = threadIdx.x + i * nthreads;  // units past the live ones are computed and dropped
+        const int rg = (v >> 2) & (RG - 1), q = v & 3;
+        float4 p[NW];
+#pragma unroll
+        for (int k = 0; k < NW; ++k) p[k] = red4[((k * RG + rg) * SL + col[i]) * 4 + q];
+        float4 sum = p[0];
+        if (S == 1 || KW == 1) {  // one level: the waves in order
+#pragma unroll
+            for (int k = 1; k < NW; ++k) sum = add4(sum, p[k]);
+        } else {  // each split's waves in order, then the splits in order
+            float4 part = p[0];
+#pragma unroll
+            for (int k = 1; k < NW; ++k) {
+                if (k % KW == 0) {
+                    sum = (k == KW) ? part : add4(sum, part);
+                    part = p[k];
+                } else {
+                    part = add4(part, p[k]);
+                }
+            }
+            sum = add4(sum, part);
+        }
+        y[i] = sum;
+    }
+}
+
+// Level 2 of the tree by the last of the NS splits of a row block to arrive:
+// its units' partials of the other splits come from the workspace
+// (device-coherent loads, all issued before any is added), its own from
+// registers; they are added in split order and Y is stored.
+template <int NS, int RG, int MU>
+__device__ inline void combine_splits(const MmArgs& a, int rb, int split, int E, int nthreads,
+                                      int U, const float4 y[MU], const bool bad[MU],
+                                      int64_t gbase, int gskip) {
+#pragma unroll
+    for (int i = 0; i < MU; ++i) {
+        const int v = threadIdx.x + i * nthreads;
+        if (v >= U) continue;
+        float4 p[NS];
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp) {
+            if (sp == split) continue;
+            const float* part = record_part(a.recs, rb, NS, E, sp) + 4 * v;
+            p[sp] = make_float4(coherent_load(part), coherent_load(part + 1),
+                                coherent_load(part + 2), coherent_load(part + 3));
+        }
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp)
+            if (sp == split) p[sp] = y[i];
+        float4 sum = p[0];
+#pragma unroll
+        for (int sp = 1; sp < NS; ++sp) sum = add4(sum, p[sp]);
+        const float nan = __builtin_nanf("");
+        store_unit<RG>(a, v, gbase, gskip, bad[i] ? make_float4(nan, nan, nan, nan) : sum);
+    }
 }
 
 // One workgroup per row block (plain: all S*KW waves) or per (row block,
-// split) (SPLIT: KW waves).  LDS: the wave partials red fp32 [waves][RG*256].
+// split) (SPLIT: KW waves).  LDS: the wave partials red, fp32, one float4 per
+// lane and (row group, column tile) of each wave.
 // FUSED: the first P workgroups are producers (see above).
 template <int RG, int CT, int D, bool NTW, bool SPLIT, bool FUSED>
 __global__ void __launch_bounds__(512)
@@ -521,7 +636,8 @@ mm_mfma_kernel(MmArgs a) {
     static_assert(D == 1 || D == 2 || D == 4, "the ring depth must divide a super-chunk");
     static_assert(RG == 1 || RG == 2 || RG == 4, "row groups per wave");
     extern __shared__ __align__(16) float red[];
-    __shared__ int last_flag;
+    __shared__ int wait_expired;
+    __shared__ int last_split;
     static_assert(CT >= 1 && CT * 16 <= kMaxColumns, "column tiles");
     constexpr int E = RG * CT * 256;  // output tile: RG row groups x 16 rows x 16*CT slots
     const int lane = threadIdx.x & 63;
@@ -557,11 +673,11 @@ mm_mfma_kernel(MmArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[rg][ct][r] = 0.0f;
 
-    // the live tokens' slots, for the output gather: read now, so that the
-    // load's latency hides behind the weight stream
-    __shared__ int tok_slot[kMaxColumns];
+    // the live tokens' slots, for the output gather: lane t of each wave
+    // holds batch_index[t], read now so that the load's latency hides behind
+    // the weight stream
     int my_slot = 0;
-    if ((int)threadIdx.x < 16 * CT && (int)threadIdx.x < a.n_live) my_slot = a.bidx[threadIdx.x];
+    if (lane < a.n_live) my_slot = a.bidx[lane];
 
     // The ring: chunk c sits in ring[c % D].  The scales of the next
     // super-chunk are loaded just before the first chunk of it, so waiting for
@@ -569,11 +685,12 @@ mm_mfma_kernel(MmArgs a) {
     Chunk<RG, CT> ring[D];
     uint32_t ws_next[RG], xs_next[CT];
     load_scales<RG>(ws_next, sc0, wsrow, gd);
+    bool poison = false;
     if (FUSED) {
         // weights first; the slots only once the producers have published them
 #pragma unroll
         for (int i = 0; i < D; ++i) load_chunk_w<RG, CT, NTW>(ring[i], c_lo + i, wrow, gq);
-        wait_for_slots(a, bid);
+        poison = wait_for_slots(a, bid, &wait_expired);
         load_slot_scales<CT>(xs_next, sc0, xsrow, a.xd_gs);
 #pragma unroll
         for (int i = 0; i < D; ++i) load_chunk_a<RG, CT>(ring[i], c_lo + i, xa, a.xq_gs);
@@ -612,97 +729,98 @@ mm_mfma_kernel(MmArgs a) {
             load_chunk<RG, CT, NTW>(ring[j % D], 4 * sc + j + D, wrow, gq, xa, a.xq_gs);
     });
 
+    // Epilogue.  Every wave writes its partial tile to LDS as [wave][row
+    // group][slot][16 rows] (lane (tq, j) writes rows 4tq .. 4tq+3 of slot
+    // 16ct + j as one float4); then each thread takes whole output units (see
+    // store_unit), reads its token's slot column of every wave's tile (all
+    // the reads issued before any add) and adds them in the tree's order:
+    // waves in order within a split, splits in order.
+    constexpr int SL = 16 * CT;  // slot columns
+    constexpr int MU = RG * CT;  // units per thread at most (n_live <= SL, >= 64 threads)
+    float4* red4 = reinterpret_cast<float4*>(red);
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                red[((w * RG + rg) * CT + ct) * 256 + r * 64 + lane] = acc[rg][ct][r];
-    if ((int)threadIdx.x < 16 * CT) tok_slot[threadIdx.x] = my_slot;
+            red4[((w * RG + rg) * SL + ct * 16 + (lane & 15)) * 4 + tq] =
+                make_float4(acc[rg][ct][0], acc[rg][ct][1], acc[rg][ct][2], acc[rg][ct][3]);
     __syncthreads();
-    if (FUSED && threadIdx.x == 0) {
-        // every wave of this workgroup is past the wait: the last workgroup
-        // to get here rearms all the counters
-        if (arrive_last(a.qdone, a.qdone_sub, bid, a.n_cons)) {
-            __hip_atomic_store(a.qflag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(a.qdone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            for (int k = 0; k < kSubCounters; ++k) {
-                __hip_atomic_store(a.qflag_sub + k * kSubStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(a.qdone_sub + k * kSubStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            for (int k = 0; k < kReadyCopies; ++k)
-                __hip_atomic_store(a.qready + k * kReadyStride, 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+    if (FUSED && threadIdx.x == 0) fused_exit(a);
+    const int nthreads = nwaves * 64;
+    const int U = a.n_live * RG * 4;
+    // this thread's units, their slot columns (lane t of every wave holds
+    // batch_index[t]; the shuffle runs in every lane) and the tree's sums
+    // over this workgroup's waves
+    int col[MU];
+    bool bad[MU];
+    float4 y[MU];
+#pragma unroll
+    for (int i = 0; i < MU; ++i) {
+        const int v = threadIdx.x + i * nthreads;
+        const int t = v < U ? v / (4 * RG) : 0;
+        const int sl = __shfl(my_slot, t);
+        bad[i] = poison || sl < 0 || sl >= SL;
+        col[i] = bad[i] ? 0 : sl;
+    }
+    {
+        const int S_here = SPLIT ? 1 : a.S;  // a split workgroup sums its KW waves only
+        switch (nwaves) {
+#define Q8_SUMS(NW) \
+            case NW: tile_sums<NW, RG, SL, MU>(red4, col, nthreads, S_here, a.KW, y); break;
+            Q8_SUMS(1) Q8_SUMS(2) Q8_SUMS(3) Q8_SUMS(4) Q8_SUMS(5) Q8_SUMS(6) Q8_SUMS(7) Q8_SUMS(8)
+#undef Q8_SUMS
+            default: break;  // more waves than a workgroup may hold: never launched
         }
     }
-
-    const int nthreads = nwaves * 64;
     if (!SPLIT) {
-        for (int o = threadIdx.x; o < E; o += nthreads) {
-            const TileOut to = tile_out<RG, CT>(a, tok_slot, o, gbase, gskip);
-            if (to.store)
-                a.Y[(int64_t)to.t * a.N + to.n] =
-                    to.bad ? __builtin_nanf("") : tree_sum(red, E, to.e, a.S, a.KW);
+#pragma unroll
+        for (int i = 0; i < MU; ++i) {
+            const int v = threadIdx.x + i * nthreads;
+            if (v < U) {
+                const float nan = __builtin_nanf("");
+                store_unit<RG>(a, v, gbase, gskip, bad[i] ? make_float4(nan, nan, nan, nan) : y[i]);
+            }
         }
         return;
     }
-    // level 1 of this split, every slot column, published in the workspace.
-    // The partials are written with device-coherent stores and the wait below
-    // makes them complete before the counter moves, so no cache has to be
-    // flushed; the last split reads them back with device-coherent loads.
+    // Level 2 across workgroups.  This split's units go to the workspace
+    // with device-coherent stores (unit v at floats 4v .. 4v+3); once every
+    // thread's stores have completed, the split arrives at its row block's
+    // counter.  The last to arrive loads the other splits' units
+    // (device-coherent loads, all issued before any is added), adds the S
+    // partials in split order, its own straight from registers, stores Y and
+    // rearms the counter.
+    static_assert(!SPLIT || CT == 1, "split execution has one column tile");
     float* mine = record_part(a.recs, rb, a.S, E, split);
-    for (int e = threadIdx.x; e < E; e += nthreads) coherent_store(mine + e, split_sum(red, E, e, 0, a.KW));
-    // every thread waits for its own stores to complete before the barrier,
-    // so the counter can only move once the whole partial is in place
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+    for (int i = 0; i < MU; ++i) {
+        const int v = threadIdx.x + i * nthreads;
+        if (v < U) {
+            // a workgroup whose wait ran out publishes NaN: the combined rows are NaN
+            const float4 o = bad[i] ? make_float4(__builtin_nanf(""), __builtin_nanf(""),
+                                                  __builtin_nanf(""), __builtin_nanf(""))
+                                    : y[i];
+            coherent_store(mine + 4 * v, o.x);
+            coherent_store(mine + 4 * v + 1, o.y);
+            coherent_store(mine + 4 * v + 2, o.z);
+            coherent_store(mine + 4 * v + 3, o.w);
+        }
+    }
+    wait_memory();
     __syncthreads();
     if (threadIdx.x == 0)
-        last_flag = __hip_atomic_fetch_add(record_counter(a.recs, rb, a.S, E), 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(a.S - 1);
+        last_split = __hip_atomic_fetch_add(record_counter(a.recs, rb, a.S, E), 1u,
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     (uint32_t)(a.S - 1);
     __syncthreads();
-    if (!last_flag) return;
-    // the last split to arrive: level 2 in split order, then rearm the counter.
-    // A thread's partials (up to kCombineOut outputs x kCombineSplits splits)
-    // are all loaded before any is added, so their memory round trips
-    // overlap instead of queueing one output after the other.
-    constexpr int kCombineOut = 4, kCombineSplits = 8;
-    if (a.S <= kCombineSplits) {
-        for (int o0 = threadIdx.x; o0 < E; o0 += kCombineOut * nthreads) {
-            TileOut to[kCombineOut];
-            float p[kCombineOut][kCombineSplits];
-#pragma unroll
-            for (int k = 0; k < kCombineOut; ++k) {
-                const int o = o0 + k * nthreads;
-                to[k] = tile_out<RG, CT>(a, tok_slot, o < E ? o : 0, gbase, gskip);
-                to[k].store = to[k].store && o < E;
-#pragma unroll
-                for (int s = 0; s < kCombineSplits; ++s)
-                    p[k][s] = (to[k].store && s < a.S)
-                                  ? coherent_load(record_part(a.recs, rb, a.S, E, s) + to[k].e)
-                                  : 0.0f;
-            }
-#pragma unroll
-            for (int k = 0; k < kCombineOut; ++k) {
-                if (!to[k].store) continue;
-                float y = p[k][0];
-#pragma unroll
-                for (int s = 1; s < kCombineSplits; ++s)
-                    if (s < a.S) y += p[k][s];
-                a.Y[(int64_t)to[k].t * a.N + to[k].n] = to[k].bad ? __builtin_nanf("") : y;
-            }
-        }
-    } else {
-        for (int o = threadIdx.x; o < E; o += nthreads) {
-            const TileOut to = tile_out<RG, CT>(a, tok_slot, o, gbase, gskip);
-            if (!to.store) continue;
-            float y = coherent_load(record_part(a.recs, rb, a.S, E, 0) + to.e);
-            for (int s = 1; s < a.S; ++s)
-                y += coherent_load(record_part(a.recs, rb, a.S, E, s) + to.e);
-            a.Y[(int64_t)to.t * a.N + to.n] = to.bad ? __builtin_nanf("") : y;
-        }
+    if (!last_split) return;
+    switch (a.S) {
+#define Q8_COMBINE(NS) \
+        case NS: combine_splits<NS, RG, MU>(a, rb, split, E, nthreads, U, y, bad, gbase, gskip); break;
+        Q8_COMBINE(2) Q8_COMBINE(3) Q8_COMBINE(4) Q8_COMBINE(5) Q8_COMBINE(6) Q8_COMBINE(7)
+        Q8_COMBINE(8)
+#undef Q8_COMBINE
+        default: break;  // more splits than the tiling makes: never launched
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(record_counter(a.recs, rb, a.S, E), 0u, __ATOMIC_RELAXED,
@@ -727,8 +845,9 @@ hipError_t launch_mfma(MmArgs a, hipStream_t st) {
     int64_t grid = cons;
     if (FUSED) {
         // producers: one lane per 8 activation values, 64*waves lanes each
+        // (none when the caller asked for no quantisation: a P of 0)
         const int64_t lanes = (int64_t)a.n_rows * a.NSC * kScBlocks * 4;
-        a.P = (int)((lanes + 64 * waves - 1) / (64 * waves));
+        if (a.P != 0) a.P = (int)((lanes + 64 * waves - 1) / (64 * waves));
         a.n_cons = (int)cons;
         grid += a.P;
     }
@@ -890,14 +1009,6 @@ Tiling choose_tiling(const Shape& s) {
         t.kw = (int)std::min<int64_t>(kw, s.NSC);
     }
     t.nt_weights = true;
-#ifdef Q8_TUNING
-    // measurement builds only: override the tiling from the environment
-    if (const char* e = getenv("Q8_RG")) t.rg = t.rg_split = atoi(e) == 4 ? 4 : atoi(e) == 2 ? 2 : 1;
-    if (const char* e = getenv("Q8_S")) t.splits = std::max(1, atoi(e));
-    if (const char* e = getenv("Q8_KW")) t.kw = std::max(1, atoi(e));
-    if (const char* e = getenv("Q8_NTW")) t.nt_weights = atoi(e) != 0;
-    if (const char* e = getenv("Q8_D")) t.ring = atoi(e) == 1 ? 1 : atoi(e) == 2 ? 2 : 4;
-#endif
     return t;
 }
 
@@ -912,20 +1023,8 @@ hipError_t launch_ct1(const MmArgs& a, int rg, bool split, int ring, bool nt_wei
     if (rg == R && ring == D)                                                      \
         return split ? launch_mfma<R, 1, D, true, true, FUSED>(a, st)              \
                      : launch_mfma<R, 1, D, true, false, FUSED>(a, st);
-#ifdef Q8_TUNING
-    // measurement builds only: plain-cached weight loads, four row groups
-    if (!nt_weights && !FUSED && ring == 4) {
-        if (rg == 2) return split ? launch_mfma<2, 1, 4, false, true>(a, st)
-                                  : launch_mfma<2, 1, 4, false, false>(a, st);
-        return split ? launch_mfma<1, 1, 4, false, true>(a, st) : launch_mfma<1, 1, 4, false, false>(a, st);
-    }
-    Q8_CT1(4, 4) Q8_CT1(4, 1)
-#endif
     (void)nt_weights;
     Q8_CT1(2, 4) Q8_CT1(2, 1) Q8_CT1(1, 4) Q8_CT1(1, 2) Q8_CT1(1, 1)
-#ifdef Q8_TUNING
-    Q8_CT1(2, 2)
-#endif
 #undef Q8_CT1
     return hipErrorInvalidValue;
 }
@@ -964,6 +1063,7 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
     a.n_live = n_live;
     a.S = t.splits;
     a.KW = t.kw;
+    a.y_vec4 = (s.N % 4 == 0 && reinterpret_cast<uintptr_t>(Y) % 16 == 0) ? 1 : 0;
     if (a.S * a.KW > a.NSC) return hipErrorInvalidValue;
     if (e == Engine::kDot4) return a.CT == 1 ? launch_dot4(a, st) : hipErrorInvalidValue;
     const bool split = workspace != nullptr && t.splits > 1;
@@ -974,18 +1074,6 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
     // more than one column tile: a shallower ring keeps the chunk operands
     // (which grow with the tiles) in registers
     if (a.CT > 1) {
-#ifdef Q8_TUNING
-        // measurement builds only: rows and ring depth of the wide tiles
-        const int mrg = getenv("Q8_MT_RG") ? atoi(getenv("Q8_MT_RG")) : rg;
-        const int md = getenv("Q8_MT_D") ? atoi(getenv("Q8_MT_D")) : 2;
-        if (mrg == 1 || mrg == 2) {
-            a.n_rb = (int)((s.G + mrg - 1) / mrg);
-#define Q8_T(C, R, D) if (a.CT == C && mrg == R && md == D) return launch_mfma<R, C, D, true, false>(a, st);
-            Q8_T(2, 1, 1) Q8_T(2, 1, 2) Q8_T(2, 1, 4) Q8_T(2, 2, 1) Q8_T(2, 2, 2) Q8_T(2, 2, 4)
-            Q8_T(4, 1, 1) Q8_T(4, 1, 2) Q8_T(4, 1, 4) Q8_T(4, 2, 1) Q8_T(4, 2, 2) Q8_T(4, 2, 4)
-#undef Q8_T
-        }
-#endif
         // measured on MI355X: many row blocks (large N) run best with one
         // row group and two chunks in flight per wave (more waves), few with
         // two row groups and four chunks
@@ -1009,7 +1097,8 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
 hipError_t launch_matmul_fused(const uint8_t* Wq, const float* X, int n_rows,
                                uint8_t* Xq, const int32_t* batch_index, int n_live,
                                const Shape& s, const Tiling& t, float* Y,
-                               void* workspace, hipStream_t st) {
+                               void* workspace, int max_spins, bool quantize,
+                               hipStream_t st) {
     MmArgs a;
     a.CT = 1;
     a.wq = Wq;
@@ -1027,13 +1116,24 @@ hipError_t launch_matmul_fused(const uint8_t* Wq, const float* X, int n_rows,
     a.n_live = n_live;
     a.S = t.splits;
     a.KW = t.kw;
+    a.y_vec4 = (s.N % 4 == 0 && reinterpret_cast<uintptr_t>(Y) % 16 == 0) ? 1 : 0;
     a.X = X;
     a.n_rows = n_rows;
-    a.qflag = static_cast<uint32_t*>(workspace);
-    a.qdone = a.qflag + 32;            // its own 128-byte line
-    a.qdone_sub = a.qflag + 64;        // 8 lines
-    a.qflag_sub = a.qflag + 64 + kSubCounters * kSubStride;  // 8 more, all in page 0
-    a.qready = a.qflag + kReadyStride;  // pages 1..kReadyCopies
+    a.max_spins = max_spins;
+    a.P = quantize ? -1 : 0;  // -1: as many producers as the slots need
+    // page 0 of the workspace: the two top counters and the timeout word,
+    // each in its own 128-byte line, then the two sets of sub-counters;
+    // pages 1 .. kReadyCopies: the flags
+    uint32_t* w32 = static_cast<uint32_t*>(workspace);
+    a.qflag = w32;
+    a.qexit = w32 + 32;
+    a.timeouts = w32 + kFusedTimeoutsOffset / 4;
+    a.qflag_sub = w32 + 96;
+    a.qexit_sub = a.qflag_sub + kSubCounters * kSubStride;
+    a.qready = w32 + kReadyStride;
+    static_assert(kFusedTimeoutsOffset == 64 * 4, "timeout word: its own line in page 0");
+    static_assert(96 + 2 * kSubCounters * kSubStride <= kReadyStride, "counters fit page 0");
+    static_assert((1 + kReadyCopies) * kReadyStride * 4 <= kFusedFlagBytes, "flag pages");
     if (a.S * a.KW > a.NSC) return hipErrorInvalidValue;
     const bool split = t.splits > 1;
     const int rg = launch_rg(s, t, split);

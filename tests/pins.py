@@ -379,8 +379,74 @@ def pin_bad_slot(orc):
     assert np.all(np.isnan(Y[[1, 2]])) and np.all(np.isnan(A[[1, 2]]))
 
 
+def edge_blocks():
+    """Blocks at the edges of the format, each with the q and binary16 bits
+    the stated rules give by hand: (name, x float32 [32], q int8 [32], d16).
+
+    * a NaN or an infinity anywhere in the block: q = 0 and the quiet NaN
+      0x7E00 as scale (so every output using the block is NaN);
+    * absmax 63 * 2^-149: absmax/127 is below half the smallest subnormal,
+      so the scale rounds to +0 and the block is the zero block;
+    * absmax 64 * 2^-149: absmax/127 rounds up to 2^-149 (64/127 > 1/2), so
+      x = k * 2^-149 gives x/d = k exactly, and binary16(2^-149) = +0;
+    * absmax 127 * 2^20: d = 2^20 exactly, beyond binary16's range, so the
+      stored scale is +infinity 0x7C00 while q = k."""
+    rng = np.random.default_rng(5)
+    out = []
+    base = (rng.standard_normal(BLOCK) * 3).astype(np.float32)
+    zero_q = np.zeros(BLOCK, dtype=np.int8)
+    for name, pos, val in (("nan", 7, np.nan), ("neg_nan", 0, -np.nan), ("inf", 31, np.inf),
+                           ("neg_inf", 12, -np.inf), ("nan_and_inf", 3, np.nan)):
+        x = base.copy()
+        x[pos] = np.float32(val)
+        if name == "nan_and_inf":
+            x[20] = np.float32(-np.inf)
+        out.append((name, x, zero_q, 0x7E00))
+    k = np.array([(-1) ** i * (i * 2 % 64) for i in range(BLOCK)], dtype=np.int64)
+    k63 = k.copy()
+    k63[5] = -63
+    out.append(("underflow_63", (k63 * 2.0 ** -149).astype(np.float32), zero_q, 0x0000))
+    k64 = k.copy()
+    k64[9] = 64
+    out.append(("smallest_nonzero_scale", (k64 * 2.0 ** -149).astype(np.float32),
+                k64.astype(np.int8), 0x0000))
+    kb = np.array([(i * 37) % 255 - 127 for i in range(BLOCK)], dtype=np.int64)
+    kb[0] = 127
+    out.append(("scale_overflows_binary16", (kb * 2.0 ** 20).astype(np.float32),
+                kb.astype(np.int8), 0x7C00))
+    for name, x, q, _ in out:
+        assert x.dtype == np.float32 and x.size == BLOCK and q.size == BLOCK, name
+    return out
+
+
+def pin_edge_blocks(orc):
+    cases = edge_blocks()
+    for name, x, q, d16 in cases:
+        qo, do = orc.quantize_rows(x[None, :])
+        assert np.array_equal(qo[0], q), (name, qo[0])
+        assert int(do[0, 0]) == d16, (name, hex(int(do[0, 0])))
+    # side by side with ordinary blocks: each block keeps its own result
+    normal = (np.arange(BLOCK, dtype=np.float32) - 16) * np.float32(0.25)
+    row = np.concatenate([np.concatenate([normal, x]) for _, x, _, _ in cases])[None, :]
+    qo, do = orc.quantize_rows(row)
+    qn, dn = orc.quantize_rows(normal[None, :])
+    for i, (name, _, q, d16) in enumerate(cases):
+        assert np.array_equal(qo[0, 64 * i:64 * i + 32], qn[0]), name
+        assert int(do[0, 2 * i]) == int(dn[0, 0]), name
+        assert np.array_equal(qo[0, 64 * i + 32:64 * i + 64], q), name
+        assert int(do[0, 2 * i + 1]) == d16, name
+    # a NaN-scaled block turns its outputs into NaN, the others stay finite
+    qw = np.ones((2, 64), dtype=np.int8)
+    dw = np.array([[0x3C00, 0x3C00], [0x3C00, 0x7E00]], dtype=np.uint16)
+    qx = np.ones((1, 64), dtype=np.int8)
+    dx = np.full((1, 2), 0x3C00, dtype=np.uint16)
+    Y, _ = orc.matmul(qw, dw, qx, dx, np.array([0], dtype=np.int32))
+    assert Y[0, 0] == 64.0 and np.isnan(Y[0, 1]), Y
+
+
 FAST_PINS = [
     pin_closed_forms,
+    pin_edge_blocks,
     pin_f16_boundaries,
     pin_f16_to_f32,
     pin_open_readings,

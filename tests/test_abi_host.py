@@ -29,7 +29,7 @@ def test_header_declares_the_abi():
     names = header_functions()
     for core in ("q8_pack_weights", "q8_quantize_acts", "q8_matmul_narrow"):
         assert core in names
-    assert len(names) == 20, names
+    assert len(names) == 21, names
 
 
 def test_every_declared_symbol_is_exported(q8):
@@ -92,6 +92,23 @@ def test_shape_limit_is_the_padded_size(q8):
     assert q8.q8_packed_weight_bytes(1 << 13, (1 << 21) - 32) > 0
     assert q8.q8_packed_weight_bytes((1 << 13) + 1, (1 << 21) - 32) == 0
     assert q8.q8_packed_weight_bytes(151936, 5120) > 0           # the largest matrix here
+
+
+@pytest.mark.parametrize("K", [32, 288, 768, 5120, 17408, 18432])
+def test_slot_buffer_is_the_packed_16_row_matrix(q8, K):
+    """The slot buffer's layout is the packed layout of a 16 x K matrix
+    (row s = slot s): its size is exactly that matrix's packed size, at any
+    slot count the multi-column calls take, and the library exports no slot
+    stride.  Slots are crafted and read through the canonical q8_0
+    import/export with N = 16 (the binding's write_act_slots and
+    read_act_slots)."""
+    assert q8.q8_act_buffer_bytes(K) == q8.q8_packed_weight_bytes(16, K)
+    for n in (16, 32, 48, 64):
+        assert q8.q8_act_buffer_bytes_n(K, n) == q8.q8_packed_weight_bytes(n, K)
+    assert not hasattr(q8.library(), "q8_act_slot_stride")
+    import inspect
+    assert "q8_pack_weights_q(q, d16, n_slots, K, Xq" in inspect.getsource(q8.write_act_slots)
+    assert "q8_unpack_weights(Xq, n_slots, K, q, d" in inspect.getsource(q8.read_act_slots)
 
 
 def test_invalid_k_has_no_slot_buffer(q8):
@@ -242,6 +259,17 @@ def test_fused_workspace_sizes(q8):
     assert q8.q8_matmul_fused_workspace_bytes(0, 5120) == 0
 
 
+def test_fused_bounded_rejects_invalid_bounds(q8):
+    lib = q8.library()
+    bad = q8.Q8_ERR_INVALID_ARG
+    need = q8.q8_matmul_fused_workspace_bytes(64, 256)
+    for spins, quantize in ((0, 1), (-1, 1), ((1 << 30) + 1, 1), (8, 2), (8, -1)):
+        assert lib.q8_matmul_narrow_fused_bounded(P, P, 16, P, P, 4, 64, 256, P, P, need, spins,
+                                                  quantize, None) == bad, (spins, quantize)
+    assert lib.q8_matmul_narrow_fused_bounded(P, P, 16, P, P, 4, 64, 256, P, P, need - 1, 8, 1,
+                                              None) == bad
+
+
 def test_fused_call_rejects_invalid_arguments(q8):
     lib = q8.library()
     bad = q8.Q8_ERR_INVALID_ARG
@@ -291,3 +319,95 @@ def test_stream_read_rejects_invalid_arguments(q8):
     assert lib.q8_stream_read(P + 8, 1024, P, None) == bad         # misaligned buffer
     assert lib.q8_stream_read(P, 1024, P + 2, None) == bad         # misaligned sink
     assert lib.q8_stream_read(P, (1 << 40) + 16, P, None) == bad   # too large
+
+
+# --------------------------------------------- binding argument checks
+#
+# The binding checks tensors before any call: dtype, size against the
+# library's own size functions and n_live * N, contiguity, and that the
+# tensor is on the current device.  These run on the CPU: the checks come in
+# that order, so host tensors of a wrong dtype or size fail before the device
+# check, and correct host tensors fail at the device check.
+
+def _t(n, dtype):
+    import torch
+    return torch.zeros(n, dtype=dtype)
+
+
+def test_binding_rejects_wrong_dtypes(q8):
+    import torch
+    N, K = 32, 256
+    wq = _t(q8.q8_packed_weight_bytes(N, K), torch.uint8)
+    xq = _t(q8.q8_act_buffer_bytes(K), torch.uint8)
+    Y = _t(4 * N, torch.float32)
+    bi = _t(4, torch.int32)
+    cases = [
+        (lambda: q8.q8_pack_weights(_t(N * K, torch.float64), N, K, wq, stream=0), "W: expected float32"),
+        (lambda: q8.q8_pack_weights_q(_t(N * K, torch.uint8), _t(N * K // 32, torch.int16), N, K, wq,
+                                      stream=0), "q: expected int8"),
+        (lambda: q8.q8_pack_weights_q(_t(N * K, torch.int8), _t(N * K // 32, torch.float32), N, K, wq,
+                                      stream=0), "d16: expected int16 or float16"),
+        (lambda: q8.q8_quantize_acts(_t(16 * K, torch.float16), 16, K, xq, stream=0), "X: expected float32"),
+        (lambda: q8.q8_matmul_narrow(wq, xq, _t(4, torch.int64), 4, N, K, Y, stream=0),
+         "batch_index: expected int32"),
+        (lambda: q8.q8_matmul_narrow(wq, xq, bi, 4, N, K, _t(4 * N, torch.float64), stream=0),
+         "Y: expected float32"),
+        (lambda: q8.q8_rope_multi(Y, 4, N, _t(4, torch.int64), 1, 8, 1e4, stream=0),
+         "pos: expected int32"),
+    ]
+    for fn, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            fn()
+
+
+def test_binding_rejects_undersized_tensors(q8):
+    import torch
+    N, K = 48, 512
+    pw = q8.q8_packed_weight_bytes(N, K)
+    ab = q8.q8_act_buffer_bytes(K)
+    wq, xq = _t(pw, torch.uint8), _t(ab, torch.uint8)
+    bi, Y = _t(5, torch.int32), _t(5 * N, torch.float32)
+    cases = [
+        (lambda: q8.q8_pack_weights(_t(N * K - 1, torch.float32), N, K, wq, stream=0), "W: holds"),
+        (lambda: q8.q8_pack_weights(_t(N * K, torch.float32), N, K, _t(pw - 1, torch.uint8), stream=0),
+         "Wq: holds"),
+        (lambda: q8.q8_unpack_weights(wq, N, K, _t(N * K, torch.int8), _t(N * K // 32 - 1, torch.int16),
+                                      stream=0), "d16: holds"),
+        (lambda: q8.q8_quantize_acts(_t(16 * K, torch.float32), 16, K, _t(ab - 16, torch.uint8),
+                                     stream=0), "Xq: holds"),
+        (lambda: q8.q8_matmul_narrow(wq, xq, _t(4, torch.int32), 5, N, K, Y, stream=0),
+         "batch_index: holds"),
+        (lambda: q8.q8_matmul_narrow(wq, xq, bi, 5, N, K, _t(5 * N - 1, torch.float32), stream=0),
+         "Y: holds"),
+        (lambda: q8.q8_matmul_narrow_noalloc(_t(pw - 16, torch.uint8), xq, bi, 5, N, K, Y, stream=0),
+         "Wq: holds"),
+        (lambda: q8.q8_matmul_multi(wq, xq, 32, bi, 5, N, K, Y, stream=0), "Xq: holds"),
+        (lambda: q8.q8_matmul_narrow_fused(wq, _t(16 * K - 1, torch.float32), 16, xq, bi, 5, N, K, Y,
+                                           _t(q8.q8_matmul_fused_workspace_bytes(N, K), torch.uint8),
+                                           stream=0), "X: holds"),
+        (lambda: q8.q8_matmul_narrow_fused(wq, _t(16 * K, torch.float32), 16, xq, bi, 5, N, K, Y,
+                                           _t(1024, torch.uint8), stream=0), "workspace: holds"),
+        (lambda: q8.q8_matmul_narrow_ws(wq, xq, bi, 5, 5120, 17408, _t(5 * 5120, torch.float32),
+                                        _t(100, torch.uint8), stream=0), "holds"),
+        (lambda: q8.q8_rope_multi(_t(3 * 100, torch.float32), 4, 100, _t(4, torch.int32), 2, 8, 1e4,
+                                  stream=0), "Y: holds"),
+        (lambda: q8.q8_stream_read(_t(1000, torch.uint8), 1024, _t(1024, torch.int32), stream=0),
+         "buf: holds"),
+    ]
+    for fn, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            fn()
+
+
+def test_binding_rejects_host_tensors_and_non_tensors(q8):
+    import torch
+    N, K = 16, 256
+    wq = _t(q8.q8_packed_weight_bytes(N, K), torch.uint8)
+    xq = _t(q8.q8_act_buffer_bytes(K), torch.uint8)
+    with pytest.raises(ValueError, match="expected a device tensor"):
+        q8.q8_matmul_narrow(wq, xq, _t(2, torch.int32), 2, N, K, _t(2 * N, torch.float32), stream=0)
+    with pytest.raises(ValueError, match="contiguous"):
+        q8.q8_matmul_narrow(wq, xq, _t(4, torch.int32)[::2], 2, N, K, _t(2 * N, torch.float32),
+                            stream=0)
+    with pytest.raises(TypeError):
+        q8.q8_matmul_narrow(wq, xq, [0, 1], 2, N, K, _t(2 * N, torch.float32), stream=0)

@@ -51,13 +51,28 @@ def test_more_than_one_gpu_is_refused():
 
 def test_steps_per_graph_divides_the_timed_steps():
     import bench
-    assert bench.steps_per_graph(4, 400) == 40
-    assert bench.steps_per_graph(4, 100) == 20
-    assert bench.steps_per_graph(4, 50) == 1      # no multiple of 4 divides 50
-    assert bench.steps_per_graph(3, 9) == 9
-    for copies, steps in ((4, 400), (4, 100), (2, 30), (5, 7)):
-        n = bench.steps_per_graph(copies, steps)
-        assert steps % n == 0 and (n == 1 or n % copies == 0)
+    assert bench.steps_per_graph(400) == 40
+    assert bench.steps_per_graph(100) == 25
+    assert bench.steps_per_graph(20) == 20
+    assert bench.steps_per_graph(7) == 7
+    assert bench.steps_per_graph(41) == 1
+    for steps in (400, 100, 30, 7, 97):
+        n = bench.steps_per_graph(steps)
+        assert steps % n == 0 and 1 <= n <= 40
+
+
+def test_each_matrix_rotates_at_least_a_gib():
+    """Per-matrix rotations of packed copies: every Qwen3-14B layer matrix
+    covers at least 1 GiB on its own (QKV 28 copies, O 39, gate+up 6, down
+    12), so per-matrix timings stream from HBM, not the 256 MB cache."""
+    import bench
+    want = {"qkv": 28, "o": 39, "gate_up": 6, "down": 12}
+    for m in wl.WORKLOADS["qwen3_layer"].matrices:
+        nbytes = m.N * (m.K // 32) * 34  # no padding on these shapes
+        c = bench.copies_for(nbytes)
+        assert c == want[m.name] and c * nbytes >= 1 << 30 > (c - 1) * nbytes, m.name
+    assert bench.copies_for(1 << 20) == bench.MAX_COPIES  # tiny matrices are capped
+    assert bench.copies_for(4 << 30) == 2
 
 
 def test_schedule_draws_every_live_batch_uniformly():

@@ -40,10 +40,11 @@ def _x(n, K, seed):
 
 
 def _counters_clear(ws, N, K):
-    """The fused counters and flags (the first 64 KB) and, for split shapes,
-    every row block's split counter are back to zero; the partial sums may
-    hold anything."""
-    if ws[:65536].any():
+    """The fused counters and flags (the first 64 KB, but the timeout word)
+    and, for split shapes, every row block's split counter are back to zero;
+    the partial sums may hold anything."""
+    t = _q8().Q8_FUSED_TIMEOUTS_OFFSET
+    if ws[:t].any() or ws[t + 4:65536].any():
         return False
     if _q8().q8_matmul_workspace_bytes(N, K) > 0:
         return split_counters_clear(ws, N, K, offset=65536)
@@ -170,3 +171,59 @@ def test_fused_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int32), Y.view(torch.int32)), rep
         assert _counters_clear(ws, N, K)
+
+
+@pytest.mark.parametrize("N,K", [(100, 800), (40, 17408), (5120, 5120), (5120, 17408)])
+def test_fused_wait_that_runs_out_is_loud(N, K):
+    """Forced from the host: no quantising workgroups and a small bound on
+    the wait.  Every kernel finishes, every output row is quiet NaN, the
+    workspace's timeout word counts the matmul workgroups, the counters are
+    rearmed, and the next normal call on the same workspace is right."""
+    q8 = _q8()
+    rng = np.random.default_rng(N + K)
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    Wq = gpu_pack(W)
+    ws = q8.zeroed_fused_workspace(N, K)
+    X = _x(16, K, seed=7)
+    Xd = to_dev(X)
+    Xq = q8.empty_act_slots(K)
+    bi = rng.permutation(16)[:9].astype(np.int32)
+    bi_d = to_dev(bi)
+    counts = []
+    for rep in range(2):
+        Y = torch.zeros((bi.size, N), dtype=torch.float32, device="cuda")
+        q8.q8_matmul_narrow_fused_bounded(Wq, Xd, 16, Xq, bi_d, bi.size, N, K, Y, ws,
+                                          max_spins=8, quantize=0)
+        torch.cuda.synchronize()
+        assert torch.isnan(Y).all(), rep
+        assert _counters_clear(ws, N, K), rep
+        counts.append(q8.fused_timeouts(ws))
+    assert counts[0] >= 1 and counts[1] == 2 * counts[0], counts
+    assert not Xq.any(), "no slot may be written without quantising workgroups"
+    Ys, slots_s = _separate(Wq, X, q8.empty_act_slots(K), bi, N, K)
+    Yf, slots_f = _fused(Wq, X, Xq, bi, N, K, ws)
+    assert np.array_equal(slots_s, slots_f)
+    assert np.array_equal(Ys.view(np.uint32), Yf.view(np.uint32))
+    assert _counters_clear(ws, N, K)
+    assert q8.fused_timeouts(ws) == counts[1], "a normal call adds no timeout"
+
+
+def test_fused_bounded_with_quantisation_is_the_fused_call():
+    """quantize = 1 with a generous bound is q8_matmul_narrow_fused."""
+    q8 = _q8()
+    N, K = 1000, 5120
+    rng = np.random.default_rng(3)
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    Wq = gpu_pack(W)
+    X = _x(16, K, seed=9)
+    bi = rng.permutation(16)[:11].astype(np.int32)
+    Yf, slots_f = _fused(Wq, X, q8.empty_act_slots(K), bi, N, K, q8.zeroed_fused_workspace(N, K))
+    ws = q8.zeroed_fused_workspace(N, K)
+    Xq = q8.empty_act_slots(K)
+    Y = torch.empty((bi.size, N), dtype=torch.float32, device="cuda")
+    q8.q8_matmul_narrow_fused_bounded(Wq, to_dev(X), 16, Xq, to_dev(bi), bi.size, N, K, Y, ws,
+                                      max_spins=1 << 22, quantize=1)
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.cpu().numpy().view(np.uint32), Yf.view(np.uint32))
+    assert np.array_equal(Xq.cpu().numpy(), slots_f)
+    assert q8.fused_timeouts(ws) == 0

@@ -82,6 +82,63 @@ def test_quantize_acts_partial_rows_leave_other_slots():
     assert np.array_equal(q[5:], q0[5:]) and np.array_equal(d[5:], d0[5:])
 
 
+def _edge_rows(n_rows, K, seed):
+    """fp32 rows of N(0,1) blocks with the format's edge blocks (a NaN or an
+    infinity in the block, scales that underflow to zero or overflow
+    binary16; the pins fix their quantisation by hand) placed at seeded
+    block positions."""
+    import pins
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((n_rows, K), dtype=np.float32)
+    KB = K // 32
+    for r in range(n_rows):
+        for _, x, _, _ in pins.edge_blocks():
+            if rng.random() < 0.6:
+                b = int(rng.integers(0, KB))
+                X[r, 32 * b:32 * b + 32] = x
+    return X
+
+
+@pytest.mark.parametrize("K", [288, 5120])
+def test_quantize_edge_blocks_bit_exact(K):
+    """NaN and infinity blocks, underflowing and overflowing scales: the
+    pre-quantiser and the packer give the oracle's bits."""
+    X = _edge_rows(16, K, seed=K)
+    Xq = gpu_quantize_acts(X)
+    q, d = slots_host(Xq, K)
+    qo, do = oracle.quantize_rows(X)
+    assert np.array_equal(q, qo)
+    assert np.array_equal(d, do)
+    W = _edge_rows(37, K, seed=K + 1)
+    qw, dw = gpu_unpack(gpu_pack(W), 37, K)
+    qwo, dwo = oracle.quantize_rows(W)
+    assert np.array_equal(qw, qwo)
+    assert np.array_equal(dw, dwo)
+
+
+def test_matmul_nan_blocks_give_nan_outputs():
+    """A weight row or an activation slot holding a NaN or an infinity gives
+    NaN outputs exactly where the oracle does; the other outputs stay within
+    tolerance."""
+    import pins
+    N, K = 48, 1024
+    rng = np.random.default_rng(9)
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    X = rng.standard_normal((16, K), dtype=np.float32)
+    nan_block = pins.edge_blocks()[0][1]
+    W[5, 64:96] = nan_block
+    X[7, 512:544] = nan_block
+    Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
+    bi = rng.permutation(16).astype(np.int32)
+    Yo, Ao = _oracle_y(W, X, bi)
+    for p in (MFMA, DOT4):
+        Y = gpu_matmul(Wq, Xq, bi, N, K, p)
+        assert np.array_equal(np.isnan(Y), np.isnan(Yo)), p
+        assert np.isnan(Yo[:, 5]).all() and np.isnan(Yo[list(bi).index(7)]).all()
+        fin = ~np.isnan(Yo)
+        assert within_tau(Y[fin], Yo[fin], Ao[fin])[0], p
+
+
 # ------------------------------------------------------------------- packer
 
 @pytest.mark.parametrize("N,K", [(1, 32), (17, 288), (100, 800), (768, 768),
@@ -98,7 +155,7 @@ def test_pack_weights_bit_exact_small(N, K):
 
 @pytest.mark.parametrize("key,idx", [("qwen3_layer", 0), ("qwen3_layer", 1),
                                      ("qwen3_layer", 2), ("qwen3_layer", 3),
-                                     ("large_dense", 1)])
+                                     ("large_dense", 0), ("large_dense", 1)])
 def test_pack_weights_bit_exact_full(key, idx):
     w = wl.WORKLOADS[key]
     m = w.matrices[idx]
@@ -419,8 +476,9 @@ def test_columns_equal_single_token_calls():
 
 def test_qwen3_layer_every_live_batch():
     """Qwen3-14B decode layer, every live batch 1..16 with a seeded random
-    batch_index, in the launch configuration the benchmark times; sampled
-    rows against the oracle, and the two engines bit-identical on all rows."""
+    batch_index, in the launch configuration the benchmark times: every row
+    against the oracle at n_live 1 and 16, sampled rows at the others, and
+    the two engines bit-identical on all rows."""
     w = wl.WORKLOADS["qwen3_layer"]
     for idx, m in enumerate(w.matrices):
         W, X = wl.workload_inputs("qwen3_layer", idx)
@@ -428,14 +486,19 @@ def test_qwen3_layer_every_live_batch():
         import quantized_weight_streaming_q8_amd as q8
         ws = q8.zeroed_workspace(m.N, m.K)
         rows = sample_rows(m.N, 96, seed=idx)
-        qw, dw = oracle.quantize_rows(W[rows])
+        qw_all, dw_all = oracle.quantize_rows(W)
+        qw, dw = qw_all[rows], dw_all[rows]
         qx, dx = oracle.quantize_rows(X)
         del W
         for n_live in w.n_live:
             bi = wl.batch_index(w.config, n_live, random=True)
             Y = gpu_matmul(Wq, Xq, bi, m.N, m.K)
-            Yo, Ao = oracle.matmul(qw, dw, qx, dx, bi)
-            ok, worst = within_tau(Y[:, rows], Yo, Ao)
+            if n_live in (1, 16):  # every row
+                Yo, Ao = oracle.matmul(qw_all, dw_all, qx, dx, bi)
+                ok, worst = within_tau(Y, Yo, Ao)
+            else:
+                Yo, Ao = oracle.matmul(qw, dw, qx, dx, bi)
+                ok, worst = within_tau(Y[:, rows], Yo, Ao)
             assert ok, (m.name, n_live, worst)
             Yw = gpu_matmul_ws(Wq, Xq, bi, m.N, m.K, ws)
             assert np.array_equal(Y.view(np.uint32), Yw.view(np.uint32)), (m.name, n_live)
@@ -447,20 +510,31 @@ def test_qwen3_layer_every_live_batch():
 
 
 def test_qwen3_head_columns():
+    """The Qwen3-14B head 5120 -> 151936: the packer bit-exact on the whole
+    matrix, every row against the oracle at n_live 16 and sampled rows at
+    1, 2, 4 and 8, and every column bit-identical to its single-token call."""
     w = wl.WORKLOADS["qwen3_head"]
     m = w.matrices[0]
     W, X = wl.workload_inputs("qwen3_head", 0)
     Wq, Xq = gpu_pack(W), gpu_quantize_acts(X)
     rows = sample_rows(m.N, 128, seed=4)
-    qw, dw = oracle.quantize_rows(W[rows])
+    qw_all, dw_all = oracle.quantize_rows(W)
     del W
+    q, d = gpu_unpack(Wq, m.N, m.K)
+    assert np.array_equal(q, qw_all) and np.array_equal(d, dw_all)
+    del q, d
+    qw, dw = qw_all[rows], dw_all[rows]
     qx, dx = oracle.quantize_rows(X)
     Y16 = None
     for n_live in w.n_live:
         bi = wl.batch_index(w.config, n_live, random=False)
         Y = gpu_matmul(Wq, Xq, bi, m.N, m.K)
-        Yo, Ao = oracle.matmul(qw, dw, qx, dx, bi)
-        ok, worst = within_tau(Y[:, rows], Yo, Ao)
+        if n_live == 16:  # every row
+            Yo, Ao = oracle.matmul(qw_all, dw_all, qx, dx, bi)
+            ok, worst = within_tau(Y, Yo, Ao)
+        else:
+            Yo, Ao = oracle.matmul(qw, dw, qx, dx, bi)
+            ok, worst = within_tau(Y[:, rows], Yo, Ao)
         assert ok, (n_live, worst)
         if n_live == 16:
             Y16 = Y

@@ -26,6 +26,10 @@ MUTANTS = {
     "absmax_without_abs": ("const float v = fabsf(x[i]);", "const float v = x[i];"),
     "drop_sign": ("q[i] = (int8_t)r;", "q[i] = (int8_t)fabsf(r);"),
     "truncate": ("float r = roundf(x[i] / d);", "float r = truncf(x[i] / d);"),
+    "nonfinite_quantised": ("        if (!(v <= FLT_MAX)) finite = 0; /* NaN or infinity */\n        else if",
+                            "        if (0) finite = 0;\n        else if"),
+    "nonfinite_inf_scale": ("        *d16 = 0x7e00u;", "        *d16 = 0x7c00u;"),
+    "underflow_divides": ("    if (d == 0.0f) {", "    if (a == 0.0f) {"),
     # binary16 conversion
     "f16_ties_away": ("if (rem > half || (rem == half && (r & 1u))) r += 1u;",
                       "if (rem >= half) r += 1u;"),
