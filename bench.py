@@ -704,10 +704,11 @@ def engine_ab(layer: Layer, n_values) -> dict:
 CAL_BYTES = 256 << 20
 
 
-def pmc_probe(key: str, launches: int, n_live: int, fused: bool) -> None:
+def pmc_probe(key: str, launches: int, n_live: int, fused: bool, columns: int = 16) -> None:
     """Every matrix of the workload's step in turn (the fused pre-quantise +
-    matmul, or the matmul alone), `launches` times each over two weight
-    copies, then the calibration copy three times."""
+    matmul, or the matmul alone; with `columns` > 16 the multi-column matmul
+    over that many slot columns, all live), `launches` times each over two
+    weight copies, then the calibration copy three times."""
     import torch
     import quantized_weight_streaming_q8_amd as q8
     w = wl.WORKLOADS[key]
@@ -718,15 +719,21 @@ def pmc_probe(key: str, launches: int, n_live: int, fused: bool) -> None:
         for P in packed:
             q8.q8_pack_weights(W, m.N, m.K, P)
         del W
-        X = torch.from_numpy(wl.activations(w.config, m.K, outliers=w.outliers)).cuda()
-        Xq = q8.empty_act_slots(m.K)
-        q8.q8_quantize_acts(X, 16, m.K, Xq)
-        Y = torch.empty((16, m.N), dtype=torch.float32, device="cuda")
+        X = torch.from_numpy(wl.activations(w.config, m.K, n_slots=columns,
+                                            outliers=w.outliers)).cuda()
+        Xq = q8.empty_act_slots(m.K, n_slots=columns)
+        q8.q8_quantize_acts_n(X, columns, m.K, Xq, columns)
+        Y = torch.empty((columns, m.N), dtype=torch.float32, device="cuda")
         ws = q8.zeroed_workspace(m.N, m.K)
         fws = q8.zeroed_fused_workspace(m.N, m.K)
+        if columns > 16:
+            bi = torch.from_numpy(wl.batch_index(w.config, columns, random=True,
+                                                 n_slots=columns)).cuda()
         torch.cuda.synchronize()
         for c in range(launches):
-            if fused:
+            if columns > 16:
+                q8.q8_matmul_multi(packed[c % 2], Xq, columns, bi, columns, m.N, m.K, Y)
+            elif fused:
                 q8.q8_matmul_narrow_fused(packed[c % 2], X, 16, Xq, bi, n_live, m.N, m.K, Y, fws)
             else:
                 q8.q8_matmul_narrow_ws(packed[c % 2], Xq, bi, n_live, m.N, m.K, Y, ws)
@@ -734,7 +741,8 @@ def pmc_probe(key: str, launches: int, n_live: int, fused: bool) -> None:
         del packed, X, Xq, Y, ws, fws
         torch.cuda.empty_cache()
         print(f"pmc probe: {launches} {'fused' if fused else 'matmul'} launches of {m.name} "
-              f"at n_live={n_live}", flush=True)
+              f"at n_live={columns if columns > 16 else n_live} ({columns} slot columns)",
+              flush=True)
     a = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1)
@@ -820,6 +828,9 @@ def main(argv=None) -> int:
                          "files of --pmc-probe runs")
     ap.add_argument("--pmc-launches", type=int, default=20,
                     help="the LAUNCHES of the --pmc-probe runs being summarised")
+    ap.add_argument("--columns", type=int, default=16, choices=(16, 32, 48, 64),
+                    help="--pmc-probe only: slot columns of the matmul (above 16: the multi-column "
+                         "matmul with every column live)")
     ap.add_argument("--fused", action="store_true",
                     help="run the step through the fused pre-quantise + matmul entry point "
                          "(one launch per matrix; default: separate launches, faster here)")
@@ -860,7 +871,7 @@ def main(argv=None) -> int:
     import torch
     torch.cuda.set_device(0)
     if args.pmc_probe:
-        pmc_probe(args.workload, args.pmc_probe, args.n_live, args.fused)
+        pmc_probe(args.workload, args.pmc_probe, args.n_live, args.fused, args.columns)
         return 0
     layer = Layer(args.workload, fused=args.fused)
     mats = layer.mats
