@@ -603,9 +603,9 @@ __device__ inline void combine_splits(const MmArgs& a, int rb, int split, int E,
 #pragma unroll
         for (int sp = 0; sp < NS; ++sp) {
             if (sp == split) continue;
-            const float* part = record_part(a.recs, rb, NS, E, sp) + 4 * v;
-            p[sp] = make_float4(coherent_load(part), coherent_load(part + 1),
-                                coherent_load(part + 2), coherent_load(part + 3));
+            const float* part = record_part(a.recs, rb, NS, E, sp) + v;
+            p[sp] = make_float4(coherent_load(part), coherent_load(part + E / 4),
+                                coherent_load(part + E / 2), coherent_load(part + 3 * (E / 4)));
         }
 #pragma unroll
         for (int sp = 0; sp < NS; ++sp)
@@ -784,13 +784,16 @@ mm_mfma_kernel(MmArgs a) {
         return;
     }
     // Level 2 across workgroups.  This split's units go to the workspace
-    // with device-coherent stores (unit v at floats 4v .. 4v+3); once every
-    // thread's stores have completed, the split arrives at its row block's
+    // with device-coherent stores, component-major (component c of unit v at
+    // float c*E/4 + v: each store instruction then covers whole cache lines,
+    // where a unit-major layout sends every line through four partial
+    // writes); once every thread's stores have completed, the split arrives at its row block's
     // counter.  The last to arrive loads the other splits' units
     // (device-coherent loads, all issued before any is added), adds the S
     // partials in split order, its own straight from registers, stores Y and
     // rearms the counter.
     static_assert(!SPLIT || CT == 1, "split execution has one column tile");
+    static_assert(kMaxSlots * RG * 4 <= E / 4, "a component block holds every unit");
     float* mine = record_part(a.recs, rb, a.S, E, split);
 #pragma unroll
     for (int i = 0; i < MU; ++i) {
@@ -800,10 +803,10 @@ mm_mfma_kernel(MmArgs a) {
             const float4 o = bad[i] ? make_float4(__builtin_nanf(""), __builtin_nanf(""),
                                                   __builtin_nanf(""), __builtin_nanf(""))
                                     : y[i];
-            coherent_store(mine + 4 * v, o.x);
-            coherent_store(mine + 4 * v + 1, o.y);
-            coherent_store(mine + 4 * v + 2, o.z);
-            coherent_store(mine + 4 * v + 3, o.w);
+            coherent_store(mine + v, o.x);
+            coherent_store(mine + E / 4 + v, o.y);
+            coherent_store(mine + E / 2 + v, o.z);
+            coherent_store(mine + 3 * (E / 4) + v, o.w);
         }
     }
     wait_memory();
