@@ -752,6 +752,107 @@ def pmc_probe(key: str, launches: int, n_live: int, fused: bool, columns: int = 
     print(f"pmc probe: 3 copies of {CAL_BYTES} B", flush=True)
 
 
+TICK_US = 0.01            # s_memrealtime: 100 MHz
+TIMELINE_MAX_WAVES = 1 << 20
+PCTS = (0, 10, 50, 90, 100)
+
+
+def _pct(a) -> list:
+    a = np.asarray(a, dtype=np.float64)
+    a = a[~np.isnan(a)]
+    return [round(float(v), 3) for v in np.percentile(a, PCTS)] if a.size else []
+
+
+def timeline_summary(recs: list, split: bool) -> dict:
+    """Phase durations (us, percentiles over every wave of every recorded
+    launch) from timeline-build records (include/q8timeline.h), each launch
+    taken from its own earliest wave start, plus each launch's span and the
+    waves per CU against when each CU's last wave ended."""
+    ph = {k: [] for k in ("start", "first_chunk", "stream", "reduce", "stream_end", "end")}
+    ph.update({k: [] for k in (("publish", "arrive", "combine", "last_tail") if split
+                               else ("y_issue", "y_done"))})
+    spans, cu_rows = [], []
+    for t in recs:
+        t = t[t[:, 0] > 0]
+        t0 = t[:, 0].min()
+        r = (t[:, :7] - t0).astype(np.float64) * TICK_US
+        r[t[:, :7] == 0] = np.nan
+        ph["start"].append(r[:, 0])
+        ph["first_chunk"].append(r[:, 1] - r[:, 0])
+        ph["stream"].append(r[:, 2] - r[:, 1])
+        ph["reduce"].append(r[:, 3] - r[:, 2])
+        ph["stream_end"].append(r[:, 2])
+        if split:
+            last = ~np.isnan(r[:, 6])
+            ph["publish"].append(r[:, 4] - r[:, 3])
+            ph["arrive"].append(r[:, 5] - r[:, 4])
+            ph["combine"].append((r[:, 6] - r[:, 5])[last])
+            ph["last_tail"].append((r[:, 6] - r[:, 2])[last])
+            end = np.where(last, r[:, 6], r[:, 5])
+        else:
+            ph["y_issue"].append(r[:, 4] - r[:, 3])
+            ph["y_done"].append(r[:, 5] - r[:, 4])
+            end = r[:, 5]
+        ph["end"].append(end)
+        spans.append(float(np.nanmax(end)))
+        hw = t[:, 7].astype(np.uint64)
+        cu = ((hw >> np.uint64(32)) & np.uint64(0xF)) * np.uint64(256) + ((hw >> np.uint64(8)) & np.uint64(0xFF))
+        keys, inv, counts = np.unique(cu, return_inverse=True, return_counts=True)
+        last_end = np.full(keys.size, -np.inf)
+        np.maximum.at(last_end, inv, end)
+        cu_rows.append((counts, last_end))
+    out = {"launches": len(recs), "waves": int((recs[0][:, 0] > 0).sum()),
+           "span_us": [round(v, 3) for v in spans], "span_us_median": round(float(np.median(spans)), 3),
+           "phases_us": {k: _pct(np.concatenate(v)) for k, v in ph.items()},
+           "percentiles": list(PCTS)}
+    counts = np.concatenate([c for c, _ in cu_rows])
+    ends = np.concatenate([e for _, e in cu_rows])
+    out["cus_used"] = int(np.median([c.size for c, _ in cu_rows]))
+    out["waves_per_cu"] = {int(n): {"cus": int((counts == n).sum() // len(recs)),
+                                    "last_end_us_median": round(float(np.median(ends[counts == n])), 3)}
+                           for n in np.unique(counts)}
+    return out
+
+
+def timeline_run(key: str, n_live: int, recorded: int = 5) -> dict:
+    """Per-wave timelines of every matrix's narrow matmul (workspace entry
+    point) from the timeline build: for each matrix, warm-up replays, then
+    `recorded` times a series of 8 back-to-back launches over the weight
+    rotation with recording on; each series leaves the records of its last
+    launch."""
+    import torch
+    import quantized_weight_streaming_q8_amd as q8
+    if not q8.TIMELINE:
+        raise RuntimeError("the timeline needs Q8_LIBRARY=timeline before the package is imported")
+    layer = Layer(key)
+    bi = layer.batch_index(n_live)
+    rec = torch.zeros(TIMELINE_MAX_WAVES * q8.Q8_STAMP_WORDS, dtype=torch.int64, device="cuda")
+    res = {}
+    for i, m in enumerate(layer.mats):
+        q8.q8_quantize_acts(layer.X[i], 16, m.K, layer.Xq[i])
+
+        def launch(c, i=i, m=m):
+            q8.q8_matmul_narrow_ws(layer.weights(i, c), layer.Xq[i], bi, n_live, m.N, m.K,
+                                   layer.Y[i], layer.ws[i])
+        n = layer.launches(i)
+        us = float(np.mean(graph_replay_us(launch, n, 3)))
+        recs = []
+        for r in range(recorded):
+            rec.zero_()
+            q8.q8_timeline_set(rec, TIMELINE_MAX_WAVES)
+            for c in range(8):
+                launch(8 * r + c)
+            q8.q8_timeline_set(None, 0)
+            torch.cuda.synchronize()
+            recs.append(rec.view(-1, q8.Q8_STAMP_WORDS).cpu().numpy().copy())
+        split = q8.q8_matmul_workspace_bytes(m.N, m.K) > 0
+        res[m.name] = dict(timeline_summary(recs, split), K=m.K, N=m.N, n_live=n_live,
+                           split=split, timeline_build_us_per_launch=round(us, 3))
+        print(f"timeline: {m.name} {m.K}->{m.N}: span {res[m.name]['span_us_median']} us "
+              f"(timeline build, graph replays: {us:.2f} us per launch)", flush=True)
+    return {"workload": key, "kernel_source_hash": kernel_source_hash(), "matrices": res}
+
+
 def _counter_rows(path: str, counter: str):
     import csv
     with open(path) as f:
@@ -804,6 +905,88 @@ def pmc_summarize(fetch_csv: str, write_csv: str, key: str, n_live: int, fused: 
     return out
 
 
+def pmc_table(path: str, key: str, launches: int, columns: int) -> dict:
+    """Per-dispatch medians of every counter in one counter_collection.csv of
+    `bench.py --pmc-probe LAUNCHES [--columns C]` (LAUNCHES matmul dispatches
+    per matrix, in the workload's order; a counter's rows of one dispatch
+    summed), with the VALU and MFMA instruction counts set against the
+    work: a term is one block's int32 dot of one row against one slot column,
+    scaled into fp32 (the kernel computes every slot column of its tiles)."""
+    import csv
+    mats = wl.WORKLOADS[key].matrices
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if "mm_mfma_kernel" not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault(int(r["Dispatch_Id"]), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ids = sorted(per)
+    if len(ids) != launches * len(mats):
+        raise SystemExit(f"{path}: {len(ids)} matmul dispatches, expected {launches} x {len(mats)}")
+    out = {"workload": key, "columns": columns, "kernel_source_hash": kernel_source_hash(),
+           "matrices": {}}
+    for j, m in enumerate(mats):
+        rows = [per[i] for i in ids[j * launches:(j + 1) * launches]]
+        med = {c: float(np.median([r[c] for r in rows])) for c in sorted(rows[0])}
+        G, KB = (m.N + 15) // 16, m.K // 32
+        terms = G * 16 * KB * columns
+        res = {"K": m.K, "N": m.N, "dispatches": len(rows), "counters_median": med,
+               "terms": terms, "mfma_expected": G * KB * (columns // 16)}
+        if "SQ_INSTS_VALU" in med:
+            res["valu_insts_per_term"] = round(med["SQ_INSTS_VALU"] * 64 / terms, 3)
+        if "SQ_INSTS_MFMA" in med and "SQ_INSTS_VALU" in med:
+            res["valu_minus_mfma_per_term"] = round(
+                (med["SQ_INSTS_VALU"] - med["SQ_INSTS_MFMA"]) * 64 / terms, 3)
+        for c in ("SQ_INSTS_VALU_CVT", "SQ_INSTS_VALU_FMA_F32", "SQ_INSTS_VALU_MUL_F32",
+                  "SQ_INSTS_VALU_ADD_F32", "SQ_INSTS_VALU_INT32", "SQ_INSTS_SALU"):
+            if c in med:
+                res[c.replace("SQ_INSTS_", "").lower() + "_per_term"] = round(med[c] * 64 / terms, 3)
+        out["matrices"][m.name] = res
+    return out
+
+
+def trace_table(trace_dir: str, prefix: str = "kt") -> str:
+    """Markdown table of a rocprofv3 --kernel-trace --output-format csv run
+    (files PREFIX_kernel_trace.csv and PREFIX_kernel_stats.csv in trace_dir):
+    the library's kernels grouped by name and launch shape, with launches
+    and the mean, median, min and max duration in us, then the library's
+    rows of the stats file as written."""
+    import csv
+    import re
+
+    def short(n):
+        n = re.sub(r"^void ", "", n).replace("q8::(anonymous namespace)::", "")
+        return re.sub(r"\(.*$", "", n)
+
+    ours = ("mm_", "quantize", "rope", "stream_read", "pack_", "unpack", "clear_scratch")
+    rows = {}
+    with open(os.path.join(trace_dir, f"{prefix}_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            n = short(r["Kernel_Name"])
+            if not n.startswith(ours):
+                continue
+            key = (n, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]), r["VGPR_Count"],
+                   r["LDS_Block_Size"])
+            rows.setdefault(key, []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    lines = ["| kernel | grid (threads) | block | VGPR_Count (trace field) | LDS B | launches | mean | "
+             "median | min | max |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for key, v in sorted(rows.items(), key=lambda kv: -sum(kv[1])):
+        n, g, b, vg, lds = key
+        lines.append(f"| `{n}` | {g} | {b} | {vg} | {lds} | {len(v)} | {np.mean(v):.2f} | "
+                     f"{np.median(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    stats = ["Name,Calls,TotalDurationNs,AverageNs,Percentage"]
+    with open(os.path.join(trace_dir, f"{prefix}_kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            n = short(r["Name"])
+            if n.startswith(ours):
+                stats.append(f'{n},{r["Calls"]},{r["TotalDurationNs"]},{r["AverageNs"]},'
+                             f'{r["Percentage"]}')
+    return ("\n".join(lines) + "\n\n" + f"{prefix}_kernel_stats.csv (rocprofv3 --stats, grouped by "
+            "kernel name only; the library's rows):\n\n```\n" + "\n".join(stats) + "\n```\n")
+
+
 # ------------------------------------------------------------------ main
 
 def main(argv=None) -> int:
@@ -826,6 +1009,13 @@ def main(argv=None) -> int:
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the per-matrix traffic summaries from two counter_collection.csv "
                          "files of --pmc-probe runs")
+    ap.add_argument("--pmc-table", metavar="CSV",
+                    help="print per-matrix medians of every counter in one counter_collection.csv "
+                         "of a --pmc-probe run (with --columns as in that run), with VALU and MFMA "
+                         "instructions per term")
+    ap.add_argument("--trace-table", metavar="DIR",
+                    help="print the markdown table of a rocprofv3 --kernel-trace --stats "
+                         "--output-format csv -o kt run written to DIR")
     ap.add_argument("--pmc-launches", type=int, default=20,
                     help="the LAUNCHES of the --pmc-probe runs being summarised")
     ap.add_argument("--columns", type=int, default=16, choices=(16, 32, 48, 64),
@@ -841,11 +1031,21 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-detail", action="store_true",
                     help="only time the CPU oracle per matrix at n_live 1 and 16, on all host "
                          "threads and on one (median of 3), and its pre-quantisation")
+    ap.add_argument("--timeline", action="store_true",
+                    help="only record per-wave timelines of each matrix's matmul with the timeline "
+                         "build (libq8narrow_timeline.so) and print their summary")
     ap.add_argument("--schedule", type=int, default=0, metavar="STEPS",
                     help="only run the workload's seeded decode schedule of this many steps "
                          "(live batch uniform on 1..16): aggregate GB/s and per-live-batch times")
     args = ap.parse_args(argv)
 
+    if args.trace_table:
+        print(trace_table(args.trace_table))
+        return 0
+    if args.pmc_table:
+        print(json.dumps(pmc_table(args.pmc_table, args.workload, args.pmc_launches, args.columns),
+                         indent=1))
+        return 0
     if args.pmc_summarize:
         print(json.dumps(pmc_summarize(*args.pmc_summarize, args.workload, args.n_live, args.fused,
                                        args.pmc_launches), indent=1))
@@ -868,8 +1068,18 @@ def main(argv=None) -> int:
                 f.write(text + "\n")
         return 0
 
+    if args.timeline:
+        os.environ["Q8_LIBRARY"] = "timeline"  # before the package's first import
     import torch
     torch.cuda.set_device(0)
+    if args.timeline:
+        res = timeline_run(args.workload, args.n_live)
+        text = json.dumps(res, indent=1)
+        print(text, flush=True)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text + "\n")
+        return 0
     if args.pmc_probe:
         pmc_probe(args.workload, args.pmc_probe, args.n_live, args.fused, args.columns)
         return 0

@@ -6,6 +6,11 @@ kernels behind the C ABI declared in ``include/q8narrow.h``; torch supplies
 device memory and the current stream.  The functions keep the C names and
 raise ``Q8Error`` on a non-OK status.  There is no fallback: if the library
 is not built, importing this package raises.
+
+With the environment variable Q8_LIBRARY=timeline set before the first
+import, the package loads the timeline build, libq8narrow_timeline.so, instead
+(same entry points and results, plus ``q8_timeline_set`` of
+``include/q8timeline.h``: per-wave real-time counter records for profiling).
 """
 
 from __future__ import annotations
@@ -17,7 +22,11 @@ import torch
 
 from . import build as _build
 
-LIB_PATH = _build.LIB_PATH
+_VARIANT = os.environ.get("Q8_LIBRARY", "")
+if _VARIANT not in ("", "timeline"):
+    raise ImportError(f"Q8_LIBRARY={_VARIANT!r}: only 'timeline' (or unset) is known")
+TIMELINE = _VARIANT == "timeline"
+LIB_PATH = _build.TIMELINE_LIB_PATH if TIMELINE else _build.LIB_PATH
 
 Q8_BLOCK = 32
 Q8_MAX_SLOTS = 16
@@ -62,6 +71,11 @@ _SIGNATURES = {
     "q8_device_supported": ([], _i32),
     "q8_status_str": ([_i32], ctypes.c_char_p),
 }
+# The timeline build's own symbol (include/q8timeline.h).
+_TIMELINE_SIGNATURES = {
+    "q8_timeline_set": ([_vp, _i64], _i32),
+}
+Q8_STAMP_WORDS = 8
 
 
 class Q8Error(RuntimeError):
@@ -76,7 +90,8 @@ def _load_library():
             f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
             "or `python quantized_weight_streaming_q8_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
-    for name, (args, res) in _SIGNATURES.items():
+    sigs = dict(_SIGNATURES, **(_TIMELINE_SIGNATURES if TIMELINE else {}))
+    for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
@@ -320,6 +335,17 @@ def q8_stream_read(buf, nbytes: int, sink, stream=None) -> None:
 
 def q8_device_supported() -> bool:
     return bool(_lib.q8_device_supported())
+
+
+def q8_timeline_set(records, max_waves: int) -> None:
+    """Timeline build only: the record buffer (int64, Q8_STAMP_WORDS per
+    wave) of the following matmul launches; None or max_waves 0 switches
+    recording off."""
+    if not TIMELINE:
+        raise Q8Error(Q8_ERR_UNSUPPORTED, "q8_timeline_set (set Q8_LIBRARY=timeline before the "
+                      "first import to load the timeline build)")
+    (r,) = _dev(_arg(records, "records", (torch.int64,), 8 * Q8_STAMP_WORDS * max(max_waves, 0)))
+    _check(_lib.q8_timeline_set(r, max_waves), "q8_timeline_set")
 
 
 # ------------------------------------------------- torch allocation helpers

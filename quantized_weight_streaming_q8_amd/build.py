@@ -1,7 +1,10 @@
-"""Build libq8narrow.so in-tree with hipcc for gfx950.
+"""Build libq8narrow.so, and its timeline build libq8narrow_timeline.so,
+in-tree with hipcc for gfx950.
 
 Flags: -O3, no fast-math, -ffp-contract=off (every fused multiply-add in the
 kernels is written out explicitly), and packed-fp32 instructions disabled.
+The timeline build adds -DQ8_TIMELINE (per-wave real-time counter records,
+include/q8timeline.h); nothing else differs.
 """
 
 from __future__ import annotations
@@ -15,6 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libq8narrow.so")
+TIMELINE_LIB_PATH = os.path.join(HERE, "libq8narrow_timeline.so")
 
 SOURCES = ["q8_pack.hip", "q8_matmul.hip", "q8_rope.hip", "q8_measure.hip", "q8_abi.hip",
            "q8_noalloc.hip"]
@@ -37,26 +41,47 @@ FLAGS = [
 ]
 
 
-def build(out: str = LIB_PATH, extra_flags: list[str] | None = None,
-          verbose: bool = False) -> str:
-    """Compile every source into one shared library at ``out``."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra_flags or []), "-shared", "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = "\n".join(
-        line for line in (res.stdout + res.stderr).splitlines()
+def _filtered(text: str) -> str:
+    return "\n".join(
+        line for line in text.splitlines()
         # hipcc's host pass does not know the device-only feature flag
         if "packed-fp32-ops" not in line and "is not a recognized feature" not in line)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
+
+
+def _start(out: str, extra_flags: list[str], verbose: bool) -> tuple:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra_flags, "-shared", "-o", tmp, *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    return proc, tmp, out
+
+
+def _finish(job: tuple, verbose: bool) -> str:
+    proc, tmp, out = job
+    text, _ = proc.communicate()
+    msgs = _filtered(text)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({proc.returncode}) building {out}:\n{msgs}")
     if verbose and msgs.strip():
         print(msgs, file=sys.stderr)
     os.replace(tmp, out)
     return out
 
 
+def build(out: str = LIB_PATH, extra_flags: list[str] | None = None,
+          verbose: bool = False) -> str:
+    """Compile every source into one shared library at ``out``."""
+    return _finish(_start(out, list(extra_flags or []), verbose), verbose)
+
+
+def build_all(verbose: bool = False) -> list[str]:
+    """The product library and its timeline build, compiled side by side."""
+    jobs = [_start(LIB_PATH, [], verbose),
+            _start(TIMELINE_LIB_PATH, ["-DQ8_TIMELINE"], verbose)]
+    return [_finish(j, verbose) for j in jobs]
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print("\n".join(build_all(verbose=True)))

@@ -12,6 +12,9 @@
 #include "q8narrow.h"
 #include "q8_internal.h"
 #include "q8_measure.h"
+#ifdef Q8_TIMELINE
+#include "q8timeline.h"
+#endif
 
 #include <atomic>
 #include <cstring>
@@ -246,6 +249,15 @@ q8_status q8_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStrea
 }
 
 int q8_device_supported(void) { return current_device_ok(); }
+
+#ifdef Q8_TIMELINE
+q8_status q8_timeline_set(uint64_t* records, int64_t max_waves) {
+    if (max_waves < 0 || (max_waves > 0 && (records == nullptr || !aligned(records, 8))))
+        return Q8_ERR_INVALID_ARG;
+    q8::set_timeline(records, max_waves);
+    return Q8_OK;
+}
+#endif
 
 const char* q8_status_str(q8_status status) {
     switch (status) {

@@ -206,6 +206,12 @@ constexpr int kFusedMaxSpins = 1 << 22;
 bool matmul_args_ok(const void* Wq, const void* Xq, const int32_t* batch_index, int n_live,
                     int64_t N, int64_t K, const float* Y);
 
+#ifdef Q8_TIMELINE
+// Timeline build: the record buffer of the following matmul launches (null
+// or waves <= 0: none).
+void set_timeline(uint64_t* buf, int64_t waves);
+#endif
+
 enum class Engine { kMfma, kDot4 };
 // workspace: nullptr for the single-workgroup evaluation of the tree, or a
 // zero-initialised buffer of workspace_bytes() for the split execution.

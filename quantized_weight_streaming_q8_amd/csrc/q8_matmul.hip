@@ -54,6 +54,9 @@
 
 #include <algorithm>
 #include <type_traits>
+#ifdef Q8_TIMELINE
+#include <mutex>
+#endif
 
 namespace q8 {
 namespace {
@@ -128,6 +131,49 @@ struct MmArgs {
     uint32_t* qexit_sub;  // kSubCounters exit counters, kSubStride apart
     uint32_t* qready;     // kReadyCopies "slots published" flags, kReadyStride apart
     uint32_t* timeouts;   // matmul workgroups whose wait ran out (never cleared here)
+#ifdef Q8_TIMELINE
+    uint64_t* tl;         // wave timeline records (null: none), kStampWords per wave
+    int64_t tl_waves;     // records the buffer holds
+#endif
+};
+
+// Per-wave timeline.  In the timeline build (Q8_TIMELINE) every wave of a
+// matmul launch reads the 100 MHz real-time counter at fixed points and lane
+// 0 writes them, with the wave's XCC and hardware ids, to a record of
+// kStampWords uint64 (wave index blockIdx.x * waves + wave); see
+// include/q8timeline.h for the fields.  In the product build every call
+// below is empty and the kernel is unchanged.
+constexpr int kStampWords = 8;
+
+struct WaveStamps {
+#ifdef Q8_TIMELINE
+    uint64_t t[kStampWords];
+    __device__ WaveStamps() {
+#pragma unroll
+        for (int i = 0; i < kStampWords; ++i) t[i] = 0;
+        t[0] = __builtin_amdgcn_s_memrealtime();
+        uint32_t hw, xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        t[7] = ((uint64_t)(xcc & 0xF) << 32) | hw;
+    }
+    __device__ void mark(int i) { t[i] = __builtin_amdgcn_s_memrealtime(); }
+    __device__ void mark_once(int i) {
+        if (t[i] == 0) mark(i);
+    }
+    // stores complete first, so that the next mark times them
+    __device__ void drain() { __builtin_amdgcn_s_waitcnt(0); }
+    __device__ void write(const MmArgs& a, int64_t wave, int lane) const {
+        if (a.tl == nullptr || lane != 0 || wave >= a.tl_waves) return;
+#pragma unroll
+        for (int i = 0; i < kStampWords; ++i) a.tl[wave * kStampWords + i] = t[i];
+    }
+#else
+    __device__ void mark(int) {}
+    __device__ void mark_once(int) {}
+    __device__ void drain() {}
+    __device__ void write(const MmArgs&, int64_t, int) const {}
+#endif
 };
 
 // Super-chunk range [lo, hi) of wave slice k of split s (NSC <= 2^16, so 32-bit
@@ -376,6 +422,7 @@ __device__ inline float coherent_load(const float* p) {
 __device__ inline void coherent_store(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
 
 // ------------------------------------------------------------------------
 // Fused pre-quantisation.  The first P workgroups of a FUSED launch quantise
@@ -633,6 +680,7 @@ mm_mfma_kernel(MmArgs a) {
         }
         bid -= a.P;
     }
+    WaveStamps st;
     static_assert(D == 1 || D == 2 || D == 4, "the ring depth must divide a super-chunk");
     static_assert(RG == 1 || RG == 2 || RG == 4, "row groups per wave");
     extern __shared__ __align__(16) float red[];
@@ -709,6 +757,7 @@ mm_mfma_kernel(MmArgs a) {
         static_for<0, 4>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             mfma_chunk<j, RG, CT>(ring[j % D], ws, xb, acc);
+            if constexpr (j == 0) st.mark_once(1);
             if constexpr ((j + D) % 4 == 0) {
                 load_scales<RG>(ws_next, sc + 1, wsrow, gd);
                 load_slot_scales<CT>(xs_next, sc + 1, xsrow, a.xd_gs);
@@ -725,10 +774,12 @@ mm_mfma_kernel(MmArgs a) {
     static_for<0, 4>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
         mfma_chunk<j, RG, CT>(ring[j % D], ws_next, xb, acc);
+        if constexpr (j == 0) st.mark_once(1);
         if constexpr (j + D < 4)
             load_chunk<RG, CT, NTW>(ring[j % D], 4 * sc + j + D, wrow, gq, xa, a.xq_gs);
     });
 
+    st.mark(2);
     // Epilogue.  Every wave writes its partial tile to LDS as [wave][row
     // group][slot][16 rows] (lane (tq, j) writes rows 4tq .. 4tq+3 of slot
     // 16ct + j as one float4); then each thread takes whole output units (see
@@ -745,6 +796,7 @@ mm_mfma_kernel(MmArgs a) {
             red4[((w * RG + rg) * SL + ct * 16 + (lane & 15)) * 4 + tq] =
                 make_float4(acc[rg][ct][0], acc[rg][ct][1], acc[rg][ct][2], acc[rg][ct][3]);
     __syncthreads();
+    st.mark(3);
     if (FUSED && threadIdx.x == 0) fused_exit(a);
     const int nthreads = nwaves * 64;
     const int U = a.n_live * RG * 4;
@@ -781,17 +833,21 @@ mm_mfma_kernel(MmArgs a) {
                 store_unit<RG>(a, v, gbase, gskip, bad[i] ? make_float4(nan, nan, nan, nan) : y[i]);
             }
         }
+        st.mark(4);
+        st.drain();
+        st.mark(5);
+        st.write(a, (int64_t)bid * nwaves + w, lane);
         return;
     }
     // Level 2 across workgroups.  This split's units go to the workspace
     // with device-coherent stores, component-major (component c of unit v at
     // float c*E/4 + v: each store instruction then covers whole cache lines,
     // where a unit-major layout sends every line through four partial
-    // writes); once every thread's stores have completed, the split arrives at its row block's
-    // counter.  The last to arrive loads the other splits' units
-    // (device-coherent loads, all issued before any is added), adds the S
-    // partials in split order, its own straight from registers, stores Y and
-    // rearms the counter.
+    // writes); once every thread's stores have completed, the split arrives
+    // at its row block's counter.  The last to arrive loads the other
+    // splits' units (device-coherent loads, all issued before any is added),
+    // adds the S partials in split order, its own straight from registers,
+    // stores Y and rearms the counter.
     static_assert(!SPLIT || CT == 1, "split execution has one column tile");
     static_assert(kMaxSlots * RG * 4 <= E / 4, "a component block holds every unit");
     float* mine = record_part(a.recs, rb, a.S, E, split);
@@ -811,12 +867,17 @@ mm_mfma_kernel(MmArgs a) {
     }
     wait_memory();
     __syncthreads();
+    st.mark(4);
     if (threadIdx.x == 0)
         last_split = __hip_atomic_fetch_add(record_counter(a.recs, rb, a.S, E), 1u,
                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                      (uint32_t)(a.S - 1);
     __syncthreads();
-    if (!last_split) return;
+    st.mark(5);
+    if (!last_split) {
+        st.write(a, (int64_t)bid * nwaves + w, lane);
+        return;
+    }
     switch (a.S) {
 #define Q8_COMBINE(NS) \
         case NS: combine_splits<NS, RG, MU>(a, rb, split, E, nthreads, U, y, bad, gbase, gskip); break;
@@ -828,6 +889,9 @@ mm_mfma_kernel(MmArgs a) {
     if (threadIdx.x == 0)
         __hip_atomic_store(record_counter(a.recs, rb, a.S, E), 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+    st.drain();
+    st.mark(6);
+    st.write(a, (int64_t)bid * nwaves + w, lane);
 }
 
 int mfma_waves(const MmArgs& a, bool split) { return split ? a.KW : a.S * a.KW; }
@@ -1044,11 +1108,32 @@ size_t workspace_bytes(const Shape& s, const Tiling& t) {
     return (size_t)(n_rb * record_bytes(t.splits, rg * 256));
 }
 
+#ifdef Q8_TIMELINE
+namespace {
+std::mutex g_tl_mu;
+uint64_t* g_tl_buf = nullptr;
+int64_t g_tl_waves = 0;
+}  // namespace
+
+void set_timeline(uint64_t* buf, int64_t waves) {
+    std::lock_guard<std::mutex> lock(g_tl_mu);
+    g_tl_buf = waves > 0 ? buf : nullptr;
+    g_tl_waves = g_tl_buf ? waves : 0;
+}
+#endif
+
 hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
                          int n_slots, const int32_t* batch_index, int n_live,
                          const Shape& s, const Tiling& t, float* Y,
                          void* workspace, hipStream_t st) {
     MmArgs a;
+#ifdef Q8_TIMELINE
+    {
+        std::lock_guard<std::mutex> lock(g_tl_mu);
+        a.tl = g_tl_buf;
+        a.tl_waves = g_tl_waves;
+    }
+#endif
     a.CT = n_slots / kMaxSlots;
     if (a.CT < 1 || a.CT * kMaxSlots != n_slots || n_slots > kMaxColumns) return hipErrorInvalidValue;
     a.wq = Wq;
@@ -1103,6 +1188,10 @@ hipError_t launch_matmul_fused(const uint8_t* Wq, const float* X, int n_rows,
                                void* workspace, int max_spins, bool quantize,
                                hipStream_t st) {
     MmArgs a;
+#ifdef Q8_TIMELINE
+    a.tl = nullptr;  // no timeline of the fused launch
+    a.tl_waves = 0;
+#endif
     a.CT = 1;
     a.wq = Wq;
     a.wd = reinterpret_cast<const uint16_t*>(Wq + s.q_bytes);

@@ -39,6 +39,50 @@ def test_every_declared_symbol_is_exported(q8):
     assert set(header_functions()) == set(q8._SIGNATURES)
 
 
+TIMELINE_HEADER = os.path.join(ROOT, "include", "q8timeline.h")
+
+
+def timeline_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(TIMELINE_HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(q8_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_timeline_build_exports_both_headers_and_product_build_only_its_own(q8):
+    """The timeline build exports every q8narrow.h entry point plus
+    q8_timeline_set; the product library does not export the latter."""
+    from quantized_weight_streaming_q8_amd import build
+    assert timeline_functions() == ["q8_timeline_set"]
+    assert set(timeline_functions()) == set(q8._TIMELINE_SIGNATURES)
+    tl = ctypes.CDLL(build.TIMELINE_LIB_PATH)
+    for name in header_functions() + timeline_functions():
+        assert hasattr(tl, name), name
+    prod = ctypes.CDLL(build.LIB_PATH)
+    assert not hasattr(prod, "q8_timeline_set")
+    text = open(TIMELINE_HEADER).read()
+    assert int(re.search(r"#define Q8_STAMP_WORDS (\d+)", text).group(1)) == q8.Q8_STAMP_WORDS
+
+
+def test_timeline_set_rejects_invalid_buffers():
+    """Host checks only (no device pointer is dereferenced): a negative
+    count, or a null or misaligned buffer with a positive count."""
+    from quantized_weight_streaming_q8_amd import build
+    tl = ctypes.CDLL(build.TIMELINE_LIB_PATH)
+    fn = tl.q8_timeline_set
+    fn.argtypes, fn.restype = [ctypes.c_void_p, ctypes.c_int64], ctypes.c_int
+    assert fn(None, -1) == 1
+    assert fn(None, 5) == 1
+    assert fn(0x1004, 5) == 1
+    assert fn(None, 0) == 0   # recording off
+    assert fn(0x1000, 0) == 0
+
+
+def test_product_binding_refuses_timeline_calls(q8):
+    if q8.TIMELINE:
+        pytest.skip("this process loaded the timeline build")
+    with pytest.raises(q8.Q8Error):
+        q8.q8_timeline_set(None, 0)
+
+
 def test_constants_agree_with_header(q8):
     text = open(HEADER).read()
     assert int(re.search(r"#define Q8_MAX_SLOTS (\d+)", text).group(1)) == q8.Q8_MAX_SLOTS == 16

@@ -2,6 +2,7 @@
 
 import os
 
+import numpy as np
 import pytest
 
 import bench
@@ -120,3 +121,42 @@ def test_traffic_is_reported_only_for_the_matrix_it_was_counted_on():
         if t is not None:  # only while the summary matches the kernel source
             alg = bench.matmul_bytes(N, K, 16)
             assert 0.995 * alg <= t <= 1.08 * alg, (key, name, t / alg)
+
+
+def _records(nw, split, ncu=256):
+    """Synthetic timeline records: wave i starts at i % 7 ticks, its phases
+    last 100, 1200, 40, 60 and 40 ticks (and 90 for the combine of every
+    fourth wave of a split shape); wave i runs on CU i % ncu."""
+    t = np.zeros((nw + 5, 8), dtype=np.int64)
+    w = np.arange(nw)
+    t[:nw, 0] = 10**9 + w % 7
+    for k, d in enumerate((100, 1200, 40, 60, 40)):
+        t[:nw, k + 1] = t[:nw, k] + d
+    if split:
+        t[:nw, 6] = np.where(w % 4 == 3, t[:nw, 5] + 90, 0)
+    cu = w % ncu
+    t[:nw, 7] = ((cu % 8) << 32) | ((cu // 8) << 8)
+    return t
+
+
+def test_timeline_summary_of_known_records():
+    s = bench.timeline_summary([_records(1280, True), _records(1280, True)], True)
+    assert s["launches"] == 2 and s["waves"] == 1280 and s["cus_used"] == 256
+    ph = s["phases_us"]
+    assert ph["first_chunk"] == [1.0] * 5 and ph["stream"] == [12.0] * 5
+    assert ph["reduce"] == [0.4] * 5 and ph["publish"] == [0.6] * 5
+    assert ph["arrive"] == [0.4] * 5 and ph["combine"] == [0.9] * 5
+    assert ph["last_tail"] == [2.3] * 5
+    assert ph["start"][0] == 0.0 and ph["start"][-1] == 0.06
+    assert s["span_us"] == [15.36, 15.36]  # latest start 6 + 100 + 1200 + 40 + 60 + 40 + 90 ticks
+    # each CU's last end, by a plain loop over the waves
+    last = {}
+    for w in range(1280):
+        end = w % 7 + 1440 + (90 if w % 4 == 3 else 0)
+        last[w % 256] = max(last.get(w % 256, 0), end)
+    med = float(np.median(list(last.values()))) / 100
+    assert s["waves_per_cu"] == {5: {"cus": 256, "last_end_us_median": round(med, 3)}}
+    p = bench.timeline_summary([_records(2176, False)], False)
+    assert p["waves_per_cu"][8]["cus"] == 128 and p["waves_per_cu"][9]["cus"] == 128
+    assert p["phases_us"]["y_issue"] == [0.6] * 5 and p["phases_us"]["y_done"] == [0.4] * 5
+    assert p["span_us_median"] == 14.46  # latest start 6 + 1440 ticks
