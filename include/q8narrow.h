@@ -152,8 +152,11 @@ q8_status q8_matmul_narrow_path(const void* Wq, const void* Xq,
  * the shape is invalid. */
 size_t q8_matmul_workspace_bytes(int64_t N, int64_t K);
 
-/* q8_matmul_narrow, executed with the K splits of every row block spread
- * over separate workgroups, which balances small-N shapes over the whole GPU.
+/* q8_matmul_narrow, executed with the K splits of row blocks spread over
+ * separate workgroups: every row block for long rows (K >= 8192), which
+ * balances small-N shapes over the whole GPU; for 1024..4400 row groups of
+ * 16 rows that are not a multiple of the GPU's 256 CUs, only the last
+ * (row groups mod 256) row blocks, so that every CU streams the same bytes.
  * The splits meet through `workspace` (device memory, 256-byte aligned, at
  * least q8_matmul_workspace_bytes(N, K) bytes): each split publishes its
  * partial sums, and the last to arrive adds them in split order.  The result
@@ -191,7 +194,8 @@ q8_status q8_matmul_narrow_ws(const void* Wq, const void* Xq,
  * Limit: shapes whose q8_matmul_workspace_bytes(N, K) exceeds
  * Q8_NOALLOC_SCRATCH_BYTES return Q8_ERR_TOO_LARGE and enqueue nothing
  * (8 MiB holds the split records of up to 1927 row groups of 16 rows, i.e.
- * N <= 30832 for the long rows that are split; shorter rows need none).
+ * N <= 30832 for the long rows (K >= 8192) whose row groups are all split;
+ * other shapes split at most 255 row groups or none).
  *
  * The first call on a device takes the array's device address and enqueues
  * a small kernel on `stream` that zero-fills it; make that first call

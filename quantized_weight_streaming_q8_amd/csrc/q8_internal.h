@@ -183,6 +183,12 @@ struct Tiling {
     int kw;           // wave slices per split (level 1)
     int ring;         // chunks in flight per wave (1, 2 or 4); no effect on the sums
     bool nt_weights;  // non-temporal loads for the weight stream
+    // seq: one wave per row block evaluates every split in turn (kw == 1),
+    // instead of a wave per split; split_from: in the split execution, the
+    // row groups before it run that way and only the rest as split
+    // workgroups.  Neither changes the sums.
+    bool seq;
+    int64_t split_from;
 };
 Tiling choose_tiling(const Shape& s);
 

@@ -115,6 +115,9 @@ struct MmArgs {
     int KB, NSC, n_live;
     int S, KW;            // summation tree: splits, wave slices per split
     int n_rb;             // row blocks (RG row groups each)
+    int n_whole;          // leading row blocks whose workgroup is one wave that evaluates
+                          // every split in turn (KW == 1); SPLIT: the rest run as S
+                          // split workgroups each
     int CT;               // slot column tiles (16 slots each)
     int y_vec4;           // N % 4 == 0 and Y 16-byte aligned: rows stored as float4
     int64_t xq_gs;        // slot buffer: bytes per 16 slots of the q region
@@ -200,18 +203,20 @@ __device__ inline float tree_sum(const float* red, int E, int e, int S, int KW) 
     return y;
 }
 
-// The workspace of a split execution is one record per row block: the
-// block's arrival counter alone in a 256-byte line, then the S split
-// partials of its E-element tile.  Every split shape runs S = 4 splits of a
-// one-row-group, one-column-tile tile (E = 256), so the records of every
-// shape have the same stride: a counter of one shape always sits where
-// every other shape keeps a counter, never where partials were.  A
-// workspace whose counters every call rearms may therefore serve matrices
-// of any shape in turn.
+// The workspace of a split execution is one record per row block that runs
+// as split workgroups: the block's arrival counter alone in a 256-byte
+// line, then room for kRecordSplits split partials of its E-element tile.
+// Every split shape runs at most kRecordSplits splits of a one-row-group,
+// one-column-tile tile (E = 256), so the records of every shape have the
+// same stride: a counter of one shape always sits where every other shape
+// keeps a counter, never where partials were.  A workspace whose counters
+// every call rearms may therefore serve matrices of any shape in turn.
 constexpr int64_t kRecordHead = 256;
+constexpr int kRecordSplits = 4;
 
 __host__ __device__ inline int64_t record_bytes(int S, int E) {
-    return kRecordHead + (int64_t)S * E * (int64_t)sizeof(float);
+    return kRecordHead + (int64_t)(S > kRecordSplits ? S : kRecordSplits) * E *
+                             (int64_t)sizeof(float);
 }
 
 __device__ inline uint32_t* record_counter(uint8_t* recs, int rb, int S, int E) {
@@ -639,7 +644,7 @@ __device__ inline void tile_sums(const float4* red4, const int col[MU], int nthr
 // (device-coherent loads, all issued before any is added), its own from
 // registers; they are added in split order and Y is stored.
 template <int NS, int RG, int MU>
-__device__ inline void combine_splits(const MmArgs& a, int rb, int split, int E, int nthreads,
+__device__ inline void combine_splits(const MmArgs& a, int rec, int split, int E, int nthreads,
                                       int U, const float4 y[MU], const bool bad[MU],
                                       int64_t gbase, int gskip) {
 #pragma unroll
@@ -650,7 +655,7 @@ __device__ inline void combine_splits(const MmArgs& a, int rb, int split, int E,
 #pragma unroll
         for (int sp = 0; sp < NS; ++sp) {
             if (sp == split) continue;
-            const float* part = record_part(a.recs, rb, NS, E, sp) + v;
+            const float* part = record_part(a.recs, rec, NS, E, sp) + v;
             p[sp] = make_float4(coherent_load(part), coherent_load(part + E / 4),
                                 coherent_load(part + E / 2), coherent_load(part + 3 * (E / 4)));
         }
@@ -669,7 +674,7 @@ __device__ inline void combine_splits(const MmArgs& a, int rb, int split, int E,
 // split) (SPLIT: KW waves).  LDS: the wave partials red, fp32, one float4 per
 // lane and (row group, column tile) of each wave.
 // FUSED: the first P workgroups are producers (see above).
-template <int RG, int CT, int D, bool NTW, bool SPLIT, bool FUSED>
+template <int RG, int CT, int D, bool NTW, bool SPLIT, bool FUSED, bool WHOLE>
 __global__ void __launch_bounds__(512)
 mm_mfma_kernel(MmArgs a) {
     int bid = (int)blockIdx.x;
@@ -691,11 +696,23 @@ mm_mfma_kernel(MmArgs a) {
     const int lane = threadIdx.x & 63;
     const int tq = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    const int nwaves = SPLIT ? a.KW : a.S * a.KW;
-    const int rb = SPLIT ? bid / a.S : bid;
-    const int split = SPLIT ? bid % a.S : w / a.KW;
-    int sc0, sc1;
-    slice_range(a.NSC, a.S, a.KW, split, SPLIT ? w : w % a.KW, sc0, sc1);
+    // A whole workgroup (the first n_whole row blocks) is one wave that
+    // streams its row block's whole rows and evaluates the S splits in turn:
+    // at each split's first super-chunk it folds the partial so far (the
+    // tree's level 2, in split order) and starts the next from zero, so its
+    // sums are those of S separate split waves.  A SPLIT launch runs the row
+    // blocks after those as S one-split workgroups each.  Only the WHOLE
+    // kernels (one row group per wave, launched when n_whole > 0) carry the
+    // code; the others are unchanged by it.
+    static_assert(!WHOLE || RG == 1, "whole workgroups stream one row group");
+    const int n_whole = WHOLE ? a.n_whole : 0;
+    const bool whole = WHOLE && bid < n_whole;
+    const int nwaves = (SPLIT || WHOLE) ? a.KW : a.S * a.KW;
+    const int piece = SPLIT && !whole ? bid - n_whole : 0;
+    const int rb = SPLIT && !whole ? n_whole + piece / a.S : bid;
+    const int split = whole ? 0 : SPLIT ? piece % a.S : w / a.KW;
+    int sc0 = 0, sc1 = a.NSC;
+    if (!whole) slice_range(a.NSC, a.S, a.KW, split, SPLIT ? w : w % a.KW, sc0, sc1);
     const int c_lo = 4 * sc0;  // this wave's chunks: [c_lo, 4 * sc1), at least one super-chunk
 
     // weights: RG consecutive row groups; the last row block may start
@@ -720,6 +737,24 @@ mm_mfma_kernel(MmArgs a) {
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[rg][ct][r] = 0.0f;
+    // a whole wave's level 2: the splits folded so far, and the super-chunk
+    // where the next split starts
+    float tot[RG][CT][4];
+    int fold_s = 1;
+    int fold_at = whole && a.S > 1 ? a.NSC / a.S : a.NSC;
+    auto fold = [&]() {
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    tot[rg][ct][r] = fold_s == 1 ? acc[rg][ct][r] : tot[rg][ct][r] + acc[rg][ct][r];
+                    acc[rg][ct][r] = 0.0f;
+                }
+        ++fold_s;
+        fold_at = fold_s < a.S ? fold_s * a.NSC / a.S : a.NSC;
+    };
 
     // the live tokens' slots, for the output gather: lane t of each wave
     // holds batch_index[t], read now so that the load's latency hides behind
@@ -750,6 +785,7 @@ mm_mfma_kernel(MmArgs a) {
     int sc = sc0;
     SlotScales<CT> xb;
     for (; sc + 1 < sc1; ++sc) {
+        if (whole && sc == fold_at) fold();
         uint32_t ws[RG];
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) ws[rg] = ws_next[rg];
@@ -770,6 +806,7 @@ mm_mfma_kernel(MmArgs a) {
         });
     }
     // the last super-chunk: its chunks are in the ring or loaded here
+    if (whole && sc == fold_at) fold();
     xb.prepare(xs_next);
     static_for<0, 4>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
@@ -779,6 +816,14 @@ mm_mfma_kernel(MmArgs a) {
             load_chunk<RG, CT, NTW>(ring[j % D], 4 * sc + j + D, wrow, gq, xa, a.xq_gs);
     });
 
+    if (whole && a.S > 1) {  // the last split's partial joins the folded ones
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[rg][ct][r] = tot[rg][ct][r] + acc[rg][ct][r];
+    }
     st.mark(2);
     // Epilogue.  Every wave writes its partial tile to LDS as [wave][row
     // group][slot][16 rows] (lane (tq, j) writes rows 4tq .. 4tq+3 of slot
@@ -815,7 +860,8 @@ mm_mfma_kernel(MmArgs a) {
         col[i] = bad[i] ? 0 : sl;
     }
     {
-        const int S_here = SPLIT ? 1 : a.S;  // a split workgroup sums its KW waves only
+        // a split or whole workgroup sums its KW waves only
+        const int S_here = (SPLIT || whole) ? 1 : a.S;
         switch (nwaves) {
 #define Q8_SUMS(NW) \
             case NW: tile_sums<NW, RG, SL, MU>(red4, col, nthreads, S_here, a.KW, y); break;
@@ -824,7 +870,7 @@ mm_mfma_kernel(MmArgs a) {
             default: break;  // more waves than a workgroup may hold: never launched
         }
     }
-    if (!SPLIT) {
+    if (!SPLIT || whole) {
 #pragma unroll
         for (int i = 0; i < MU; ++i) {
             const int v = threadIdx.x + i * nthreads;
@@ -850,7 +896,8 @@ mm_mfma_kernel(MmArgs a) {
     // stores Y and rearms the counter.
     static_assert(!SPLIT || CT == 1, "split execution has one column tile");
     static_assert(kMaxSlots * RG * 4 <= E / 4, "a component block holds every unit");
-    float* mine = record_part(a.recs, rb, a.S, E, split);
+    const int rec = rb - n_whole;  // records cover the split row blocks only
+    float* mine = record_part(a.recs, rec, a.S, E, split);
 #pragma unroll
     for (int i = 0; i < MU; ++i) {
         const int v = threadIdx.x + i * nthreads;
@@ -869,7 +916,7 @@ mm_mfma_kernel(MmArgs a) {
     __syncthreads();
     st.mark(4);
     if (threadIdx.x == 0)
-        last_split = __hip_atomic_fetch_add(record_counter(a.recs, rb, a.S, E), 1u,
+        last_split = __hip_atomic_fetch_add(record_counter(a.recs, rec, a.S, E), 1u,
                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                      (uint32_t)(a.S - 1);
     __syncthreads();
@@ -880,21 +927,23 @@ mm_mfma_kernel(MmArgs a) {
     }
     switch (a.S) {
 #define Q8_COMBINE(NS) \
-        case NS: combine_splits<NS, RG, MU>(a, rb, split, E, nthreads, U, y, bad, gbase, gskip); break;
+        case NS: combine_splits<NS, RG, MU>(a, rec, split, E, nthreads, U, y, bad, gbase, gskip); break;
         Q8_COMBINE(2) Q8_COMBINE(3) Q8_COMBINE(4) Q8_COMBINE(5) Q8_COMBINE(6) Q8_COMBINE(7)
         Q8_COMBINE(8)
 #undef Q8_COMBINE
         default: break;  // more splits than the tiling makes: never launched
     }
     if (threadIdx.x == 0)
-        __hip_atomic_store(record_counter(a.recs, rb, a.S, E), 0u, __ATOMIC_RELAXED,
+        __hip_atomic_store(record_counter(a.recs, rec, a.S, E), 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     st.drain();
     st.mark(6);
     st.write(a, (int64_t)bid * nwaves + w, lane);
 }
 
-int mfma_waves(const MmArgs& a, bool split) { return split ? a.KW : a.S * a.KW; }
+int mfma_waves(const MmArgs& a, bool split) {
+    return (split || a.n_whole > 0) ? a.KW : a.S * a.KW;
+}
 
 size_t mfma_lds_bytes(const MmArgs& a, int rg, int ct, bool split) {
     return (size_t)mfma_waves(a, split) * rg * ct * 256 * sizeof(float);
@@ -902,13 +951,16 @@ size_t mfma_lds_bytes(const MmArgs& a, int rg, int ct, bool split) {
 
 int mfma_max_waves(int) { return 8; }  // 512 threads: 256 VGPRs per lane
 
-template <int RG, int CT, int D, bool NTW, bool SPLIT, bool FUSED = false>
+template <int RG, int CT, int D, bool NTW, bool SPLIT, bool FUSED = false, bool WHOLE = false>
 hipError_t launch_mfma(MmArgs a, hipStream_t st) {
     const int waves = mfma_waves(a, SPLIT);
     const size_t lds = mfma_lds_bytes(a, RG, CT, SPLIT);
     if (lds > kMaxLds || waves > mfma_max_waves(RG) || a.G < RG || a.CT != CT)
         return hipErrorInvalidValue;
-    const int64_t cons = SPLIT ? (int64_t)a.n_rb * a.S : a.n_rb;
+    if (a.n_whole < 0 || a.n_whole > a.n_rb || (a.n_whole > 0) != WHOLE ||
+        (WHOLE && a.KW != 1) || (!SPLIT && a.n_whole != 0 && a.n_whole != a.n_rb))
+        return hipErrorInvalidValue;
+    const int64_t cons = SPLIT ? a.n_whole + (int64_t)(a.n_rb - a.n_whole) * a.S : a.n_rb;
     int64_t grid = cons;
     if (FUSED) {
         // producers: one lane per 8 activation values, 64*waves lanes each
@@ -918,7 +970,7 @@ hipError_t launch_mfma(MmArgs a, hipStream_t st) {
         a.n_cons = (int)cons;
         grid += a.P;
     }
-    hipLaunchKernelGGL((mm_mfma_kernel<RG, CT, D, NTW, SPLIT, FUSED>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((mm_mfma_kernel<RG, CT, D, NTW, SPLIT, FUSED, WHOLE>), dim3((unsigned)grid),
                        dim3(64 * waves), lds, st, a);
     return hipGetLastError();
 }
@@ -1051,11 +1103,23 @@ Tiling choose_tiling(const Shape& s) {
     //    gate+up 5120->34816 at 2.  Past kInFlightKB row groups even depth 1
     //    is too much: two row groups per wave then halve the waves (a
     //    152k-row head);
-    //  * never more wave slices than super-chunks.
+    //  * never more wave slices than super-chunks;
+    //  * one wave per row group leaves the CUs unevenly loaded when the row
+    //    groups are not a multiple of the 256 CUs: with gate+up's 2176, 128
+    //    CUs stream 9 row groups and 128 stream 8, and the kernel lasts as
+    //    long as the 9.  Then the tree has S = min(4, 256 / r, NSC) splits
+    //    (r = G mod 256, S >= 2) and the split execution runs the first
+    //    G - r row groups as one wave each that evaluates the splits in turn
+    //    and only the last r as S one-split workgroups each: at most one
+    //    piece per CU, dispatched after the whole rows.  Every other
+    //    execution evaluates the same splits in one wave per row group.
     constexpr int64_t kInFlightKB = 4400;
+    constexpr int64_t kCUs = 256;  // MI355X compute units
     Tiling t;
     t.rg = s.G >= 2 ? 2 : 1;
     t.ring = 4;
+    t.seq = false;
+    t.split_from = 0;
     if (s.NSC >= 32) {
         t.splits = 4;
         t.kw = 1;
@@ -1068,6 +1132,13 @@ Tiling choose_tiling(const Shape& s) {
             if (s.G <= kInFlightKB) {
                 t.rg = 1;
                 t.ring = 3 * s.G <= kInFlightKB ? 4 : 3 * s.G <= 2 * kInFlightKB ? 2 : 1;
+                const int64_t r = s.G % kCUs;
+                const int64_t st = r == 0 ? 1 : std::min<int64_t>({4, kCUs / r, s.NSC});
+                if (st >= 2) {
+                    t.splits = (int)st;
+                    t.seq = true;
+                    t.split_from = s.G - r;
+                }
             } else {
                 t.ring = 1;
             }
@@ -1087,11 +1158,17 @@ template <bool FUSED>
 hipError_t launch_ct1(const MmArgs& a, int rg, bool split, int ring, bool nt_weights,
                       hipStream_t st) {
 #define Q8_CT1(R, D)                                                               \
-    if (rg == R && ring == D)                                                      \
+    if (rg == R && ring == D && a.n_whole == 0)                                    \
         return split ? launch_mfma<R, 1, D, true, true, FUSED>(a, st)              \
                      : launch_mfma<R, 1, D, true, false, FUSED>(a, st);
+#define Q8_CT1_WHOLE(D)                                                            \
+    if (rg == 1 && ring == D && a.n_whole > 0)                                     \
+        return split ? launch_mfma<1, 1, D, true, true, FUSED, true>(a, st)        \
+                     : launch_mfma<1, 1, D, true, false, FUSED, true>(a, st);
     (void)nt_weights;
     Q8_CT1(2, 4) Q8_CT1(2, 1) Q8_CT1(1, 4) Q8_CT1(1, 2) Q8_CT1(1, 1)
+    Q8_CT1_WHOLE(4) Q8_CT1_WHOLE(2) Q8_CT1_WHOLE(1)
+#undef Q8_CT1_WHOLE
 #undef Q8_CT1
     return hipErrorInvalidValue;
 }
@@ -1104,7 +1181,7 @@ int launch_rg(const Shape& s, const Tiling& t, bool split) {
 size_t workspace_bytes(const Shape& s, const Tiling& t) {
     if (t.splits <= 1) return 0;
     const int rg = launch_rg(s, t, true);
-    const int64_t n_rb = (s.G + rg - 1) / rg;
+    const int64_t n_rb = (s.G + rg - 1) / rg - t.split_from / rg;  // split row blocks
     return (size_t)(n_rb * record_bytes(t.splits, rg * 256));
 }
 
@@ -1153,12 +1230,15 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
     a.KW = t.kw;
     a.y_vec4 = (s.N % 4 == 0 && reinterpret_cast<uintptr_t>(Y) % 16 == 0) ? 1 : 0;
     if (a.S * a.KW > a.NSC) return hipErrorInvalidValue;
+    a.n_whole = 0;
     if (e == Engine::kDot4) return a.CT == 1 ? launch_dot4(a, st) : hipErrorInvalidValue;
     const bool split = workspace != nullptr && t.splits > 1;
     if (split && a.CT != 1) return hipErrorInvalidValue;
     const int rg = launch_rg(s, t, split);
     a.n_rb = (int)((s.G + rg - 1) / rg);
     a.recs = split ? static_cast<uint8_t*>(workspace) : nullptr;
+    if (t.split_from % rg != 0) return hipErrorInvalidValue;
+    a.n_whole = split ? (int)(t.split_from / rg) : t.seq ? a.n_rb : 0;
     // more than one column tile: a shallower ring keeps the chunk operands
     // (which grow with the tiles) in registers
     if (a.CT > 1) {
@@ -1167,9 +1247,11 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
         // two row groups and four chunks
         const bool wide = (s.G + 1) / 2 >= 512 || rg == 1;
         a.n_rb = (int)(wide ? s.G : (s.G + 1) / 2);
+        a.n_whole = (t.seq && wide) ? a.n_rb : 0;  // else S*KW waves: the same tree
 #define Q8_LAUNCH_CT(C, D2)                                                     \
     case C:                                                                     \
-        return wide ? launch_mfma<1, C, 2, true, false>(a, st)                  \
+        return wide ? (a.n_whole > 0 ? launch_mfma<1, C, 2, true, false, false, true>(a, st) \
+                                     : launch_mfma<1, C, 2, true, false>(a, st))            \
                     : launch_mfma<2, C, D2, true, false>(a, st);
         switch (a.CT) {
             Q8_LAUNCH_CT(2, 4)
@@ -1231,6 +1313,8 @@ hipError_t launch_matmul_fused(const uint8_t* Wq, const float* X, int n_rows,
     const int rg = launch_rg(s, t, split);
     a.n_rb = (int)((s.G + rg - 1) / rg);
     a.recs = split ? static_cast<uint8_t*>(workspace) + kFusedFlagBytes : nullptr;
+    if (t.split_from % rg != 0) return hipErrorInvalidValue;
+    a.n_whole = (int)(t.split_from / rg);
     // 4 chunks in flight whatever the tiling says: the weights a wave puts in
     // flight before it waits for the slots are what hides that wait (the
     // ring depth does not change the sums)

@@ -108,13 +108,16 @@ def sample_rows(N: int, n: int, seed: int) -> np.ndarray:
     return rows.astype(np.int64)
 
 
+RECORD_BYTES = 256 + 4 * 1024  # counter line + room for 4 partial 16x16 fp32 tiles
+
+
 def split_counters_clear(ws, N: int, K: int, offset: int = 0) -> bool:
-    """True if every row block's arrival counter in a split workspace (from
-    byte `offset` on) is zero.  The workspace is one equal-sized record per
-    row block of 16 rows, each starting with its counter's 256-byte line."""
+    """True if every split row block's arrival counter in a split workspace
+    (from byte `offset` on) is zero.  The workspace is one record of
+    RECORD_BYTES per row block of 16 rows that runs as split workgroups,
+    each starting with its counter's 256-byte line."""
     nbytes = q8().q8_matmul_workspace_bytes(N, K)
-    n_rb = -(-N // 16)
-    rec = nbytes // n_rb
-    assert rec * n_rb == nbytes and rec > 256
-    heads = ws[offset:offset + nbytes].view(n_rb, rec)[:, :256]
+    n_rec = nbytes // RECORD_BYTES
+    assert n_rec * RECORD_BYTES == nbytes and 1 <= n_rec <= -(-N // 16)
+    heads = ws[offset:offset + nbytes].view(n_rec, RECORD_BYTES)[:, :256]
     return not heads.any()

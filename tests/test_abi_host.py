@@ -247,6 +247,14 @@ def test_workspace_sizes(q8):
     assert q8.q8_matmul_workspace_bytes(151936, 5120) == 0
     assert q8.q8_matmul_workspace_bytes(0, 5120) == 0
     assert q8.q8_matmul_workspace_bytes(16, 32) == 0  # one super-chunk: no split
+    # 1024..4400 row groups, not a multiple of the 256 CUs: only the last
+    # (G mod 256) row groups run as split workgroups, one record each
+    assert q8.q8_matmul_workspace_bytes(34816, 5120) == 128 * rec   # gate+up: 2176 = 8*256 + 128
+    assert q8.q8_matmul_workspace_bytes(18432, 7168) == 128 * rec   # 1152 = 4*256 + 128
+    assert q8.q8_matmul_workspace_bytes(17408, 5120) == 64 * rec    # 1088: 64 row groups, 4 splits
+    assert q8.q8_matmul_workspace_bytes(16391, 5120) == 1 * rec     # 1025: one ragged row group
+    assert q8.q8_matmul_workspace_bytes(32768, 5120) == 0           # 2048 = 8*256
+    assert q8.q8_matmul_workspace_bytes(16 * (1024 + 129), 5120) == 0  # r = 129: one split only
 
 
 def test_ws_entry_point_rejects_a_missing_or_small_workspace(q8):

@@ -211,8 +211,12 @@ def test_matmul_ragged_shapes(N, K):
 # Large ragged shapes that reach each tiling the default rule picks for 1024+
 # row groups: one row group per wave with 4 (G <= 1466), 2 (G <= 2933) or 1
 # (G <= 4400) chunks in flight, and two row groups per wave past 4400; N is
-# not a multiple of 16 and K leaves the last super-chunk partly empty.
-@pytest.mark.parametrize("N,K", [(16391, 4128), (32005, 800), (48003, 1056), (72009, 800)])
+# not a multiple of 16 and K leaves the last super-chunk partly empty.  For
+# G mod 256 = r in 1..128 the tree has min(4, 256 / r, NSC) splits, and the
+# workspace entry point runs only the last r row groups as split workgroups:
+# r = 1 (4 splits), 100 (2 splits), 64 (4 splits); 209 and 185 are not split.
+@pytest.mark.parametrize("N,K", [(16391, 4128), (32005, 800), (48003, 1056), (72009, 800),
+                                 (17981, 2080), (17405, 1056)])
 def test_matmul_large_ragged_shapes(N, K):
     rng = np.random.default_rng(N - K)
     W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
@@ -435,7 +439,9 @@ def test_one_workspace_serves_every_shape():
     a shape with more row blocks would find them there)."""
     import quantized_weight_streaming_q8_amd as q8
     rng = np.random.default_rng(41)
-    shapes = [(3000, 8448), (600, 9024), (2000, 8192)]  # 188, 38, 125 row groups
+    # 188, 38, 125 row groups, all split; then 1088 and 1124 row groups whose
+    # last 64 and 100 are split (4 and 2 splits)
+    shapes = [(3000, 8448), (600, 9024), (2000, 8192), (17405, 1056), (17981, 2080)]
     mats = []
     for N, K in shapes:
         assert q8.q8_matmul_workspace_bytes(N, K) > 0, (N, K)
@@ -444,7 +450,7 @@ def test_one_workspace_serves_every_shape():
         mats.append((N, K, gpu_pack(W), gpu_quantize_acts(X)))
     nbytes = max(q8.q8_matmul_workspace_bytes(N, K) for N, K in shapes)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    for rep, i in enumerate((0, 1, 2, 0, 1, 2, 1)):
+    for rep, i in enumerate((0, 1, 3, 2, 4, 0, 3, 1, 2, 4, 1)):
         N, K, Wq, Xq = mats[i]
         bi = rng.permutation(16)[: 1 + rep * 2].astype(np.int32)
         Yp = gpu_matmul(Wq, Xq, bi, N, K)

@@ -71,9 +71,11 @@ def test_noalloc_repeated_and_unsplit_shapes():
     """Calls on split and unsplit shapes in turn, each with its own live
     batch, keep giving the workspace entry point's bits."""
     rng = np.random.default_rng(77)
-    mats = [(40, 17408), (2304, 5120), (600, 9024), (17, 288)]
+    # split, unsplit, split, unsplit, and two shapes whose last 64 / 100 row
+    # groups are split (1088 and 1124 row groups)
+    mats = [(40, 17408), (2304, 5120), (600, 9024), (17, 288), (17405, 1056), (17981, 2080)]
     data = [(N, K) + _inputs(N, K, seed=300 + j)[2:] for j, (N, K) in enumerate(mats)]
-    for rep, j in enumerate((0, 1, 2, 3, 2, 0)):
+    for rep, j in enumerate((0, 1, 4, 2, 3, 5, 2, 0, 4)):
         N, K, Wq, Xq = data[j]
         bi = rng.permutation(16)[: 1 + (rep * 5) % 16].astype(np.int32)
         Yn, Yw = _both(Wq, Xq, bi, N, K)
