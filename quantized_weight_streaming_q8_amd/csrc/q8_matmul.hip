@@ -784,26 +784,33 @@ mm_mfma_kernel(MmArgs a) {
     }
     int sc = sc0;
     SlotScales<CT> xb;
-    for (; sc + 1 < sc1; ++sc) {
-        if (whole && sc == fold_at) fold();
-        uint32_t ws[RG];
+    // All super-chunks but the last, in runs that end where a whole wave
+    // folds (between runs, never inside the loop body: a test there is
+    // if-converted into selects on every accumulator, every turn).
+    for (;;) {
+        const int run_end = whole && fold_at < sc1 - 1 ? fold_at : sc1 - 1;
+        for (; sc < run_end; ++sc) {
+            uint32_t ws[RG];
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg) ws[rg] = ws_next[rg];
-        xb.prepare(xs_next);
-        static_for<0, 4>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            mfma_chunk<j, RG, CT>(ring[j % D], ws, xb, acc);
-            if constexpr (j == 0) st.mark_once(1);
-            if constexpr ((j + D) % 4 == 0) {
-                load_scales<RG>(ws_next, sc + 1, wsrow, gd);
-                load_slot_scales<CT>(xs_next, sc + 1, xsrow, a.xd_gs);
-            }
-            load_chunk<RG, CT, NTW>(ring[j % D], 4 * sc + j + D, wrow, gq, xa, a.xq_gs);
-            // keep each chunk's loads right after its dot: left alone, the
-            // scheduler sinks all the chunks' loads to the end of the turn,
-            // and every turn then waits a full memory latency
-            __builtin_amdgcn_sched_barrier(0);
-        });
+            for (int rg = 0; rg < RG; ++rg) ws[rg] = ws_next[rg];
+            xb.prepare(xs_next);
+            static_for<0, 4>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                mfma_chunk<j, RG, CT>(ring[j % D], ws, xb, acc);
+                if constexpr (j == 0) st.mark_once(1);
+                if constexpr ((j + D) % 4 == 0) {
+                    load_scales<RG>(ws_next, sc + 1, wsrow, gd);
+                    load_slot_scales<CT>(xs_next, sc + 1, xsrow, a.xd_gs);
+                }
+                load_chunk<RG, CT, NTW>(ring[j % D], 4 * sc + j + D, wrow, gq, xa, a.xq_gs);
+                // keep each chunk's loads right after its dot: left alone, the
+                // scheduler sinks all the chunks' loads to the end of the turn,
+                // and every turn then waits a full memory latency
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+        if (!whole || sc >= sc1 - 1) break;
+        fold();  // sc is the next split's first super-chunk
     }
     // the last super-chunk: its chunks are in the ring or loaded here
     if (whole && sc == fold_at) fold();
@@ -1085,6 +1092,10 @@ hipError_t launch_dot4(const MmArgs& a, hipStream_t st) {
 
 }  // namespace
 
+// Weights in flight over the whole GPU at which the stream runs fastest
+// (measured on MI355X; see choose_tiling).
+constexpr int64_t kInFlightKB = 4400;
+
 Tiling choose_tiling(const Shape& s) {
     // Rules measured on MI355X over the model-shaped matrices (K 5120..18432,
     // N 5120..151936):
@@ -1113,7 +1124,6 @@ Tiling choose_tiling(const Shape& s) {
     //    and only the last r as S one-split workgroups each: at most one
     //    piece per CU, dispatched after the whole rows.  Every other
     //    execution evaluates the same splits in one wave per row group.
-    constexpr int64_t kInFlightKB = 4400;
     constexpr int64_t kCUs = 256;  // MI355X compute units
     Tiling t;
     t.rg = s.G >= 2 ? 2 : 1;
@@ -1247,7 +1257,13 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
         // two row groups and four chunks
         const bool wide = (s.G + 1) / 2 >= 512 || rg == 1;
         a.n_rb = (int)(wide ? s.G : (s.G + 1) / 2);
-        a.n_whole = (t.seq && wide) ? a.n_rb : 0;  // else S*KW waves: the same tree
+        // a tree of S splits runs as one wave per split (S waves per row
+        // block, the same sums) unless that puts well over kInFlightKB of
+        // weights in flight (2 chunks of 1 KB per wave): measured, 7168->18432
+        // at 32 columns 34.4 against 44.0 us with whole-row waves, gate+up
+        // 41.2 whole against 46.2 us
+        const bool split_waves = 2 * (int64_t)a.n_rb * t.splits <= 3 * kInFlightKB / 2;
+        a.n_whole = (t.seq && wide && !split_waves) ? a.n_rb : 0;
 #define Q8_LAUNCH_CT(C, D2)                                                     \
     case C:                                                                     \
         return wide ? (a.n_whole > 0 ? launch_mfma<1, C, 2, true, false, false, true>(a, st) \
