@@ -771,7 +771,7 @@ def timeline_summary(recs: list, split: bool) -> dict:
     ph = {k: [] for k in ("start", "first_chunk", "stream", "reduce", "stream_end", "end")}
     ph.update({k: [] for k in (("publish", "arrive", "combine", "last_tail") if split
                                else ("y_issue", "y_done"))})
-    spans, cu_rows = [], []
+    spans, cu_rows, xcc_rows = [], [], []
     for t in recs:
         t = t[t[:, 0] > 0]
         t0 = t[:, 0].min()
@@ -796,6 +796,7 @@ def timeline_summary(recs: list, split: bool) -> dict:
         ph["end"].append(end)
         spans.append(float(np.nanmax(end)))
         hw = t[:, 7].astype(np.uint64)
+        xcc_rows.append(((hw >> np.uint64(32)) & np.uint64(0xF)).astype(np.int64))
         cu = ((hw >> np.uint64(32)) & np.uint64(0xF)) * np.uint64(256) + ((hw >> np.uint64(8)) & np.uint64(0xFF))
         keys, inv, counts = np.unique(cu, return_inverse=True, return_counts=True)
         last_end = np.full(keys.size, -np.inf)
@@ -811,6 +812,14 @@ def timeline_summary(recs: list, split: bool) -> dict:
     out["waves_per_cu"] = {int(n): {"cus": int((counts == n).sum() // len(recs)),
                                     "last_end_us_median": round(float(np.median(ends[counts == n])), 3)}
                            for n in np.unique(counts)}
+    xcc = np.concatenate(xcc_rows)
+    end_all = np.concatenate(ph["end"])
+    se_all = np.concatenate(ph["stream_end"])
+    out["per_xcc"] = {int(x): {"waves": int((xcc == x).sum() // len(recs)),
+                               "stream_end_us_p50": round(float(np.nanmedian(se_all[xcc == x])), 3),
+                               "end_us_p50": round(float(np.nanmedian(end_all[xcc == x])), 3),
+                               "end_us_max": round(float(np.nanmax(end_all[xcc == x])), 3)}
+                      for x in np.unique(xcc)}
     return out
 
 

@@ -156,6 +156,8 @@ def test_timeline_summary_of_known_records():
         last[w % 256] = max(last.get(w % 256, 0), end)
     med = float(np.median(list(last.values()))) / 100
     assert s["waves_per_cu"] == {5: {"cus": 256, "last_end_us_median": round(med, 3)}}
+    assert {x: v["waves"] for x, v in s["per_xcc"].items()} == {x: 160 for x in range(8)}
+    assert s["per_xcc"][3]["end_us_max"] == 15.36 and s["per_xcc"][0]["end_us_max"] == 14.46
     p = bench.timeline_summary([_records(2176, False)], False)
     assert p["waves_per_cu"][8]["cus"] == 128 and p["waves_per_cu"][9]["cus"] == 128
     assert p["phases_us"]["y_issue"] == [0.6] * 5 and p["phases_us"]["y_done"] == [0.4] * 5
