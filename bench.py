@@ -522,11 +522,25 @@ def cpu_baseline(key: str, n_live: int, seconds: float = 10.0):
     }
 
 
+def _median_wall(fn, runs: int, min_s: float = 0.2, most: int = 200) -> float:
+    """Median wall time of fn() over at least `runs` timed calls (more, up to
+    `most`, until min_s seconds have been timed), after one untimed call: on
+    small matrices a single call is shorter than the host's thread wake-ups."""
+    fn()
+    ts = []
+    while len(ts) < runs or (sum(ts) < min_s and len(ts) < most):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
 def cpu_detail(key: str, runs: int = 3) -> dict:
     """The oracle as it stands, per matrix of the workload: its matmul at
     n_live 1 and 16, on all the host threads OpenMP uses and on one, each the
-    median wall time of `runs` runs; and its pre-quantisation of the 16 slots
-    per K, timed separately (all threads)."""
+    median wall time of at least `runs` runs after an untimed one; and its
+    pre-quantisation of the 16 slots per K, timed the same way (all
+    threads)."""
     import oracle
     orc = oracle.get()
     w = wl.WORKLOADS[key]
@@ -542,12 +556,7 @@ def cpu_detail(key: str, runs: int = 3) -> dict:
             orc.set_num_threads(threads)
             for n in (1, 16):
                 bi = wl.batch_index(w.config, n, random=w.random_batch_index)
-                ts = []
-                for _ in range(runs):
-                    t0 = time.perf_counter()
-                    orc.matmul(qw, dw, qx, dx, bi)
-                    ts.append(time.perf_counter() - t0)
-                t = float(np.median(ts))
+                t = _median_wall(lambda: orc.matmul(qw, dw, qx, dx, bi), runs)
                 rec[f"threads={threads} n_live={n}"] = {
                     "ms": round(t * 1e3, 2), "GBps": round(matmul_bytes(m.N, m.K, n) / t / 1e9, 4)}
             print(f"# oracle {m.name} threads={threads}: "
@@ -556,12 +565,7 @@ def cpu_detail(key: str, runs: int = 3) -> dict:
         orc.set_num_threads(all_threads)
         out["matrices"][m.name] = {"K": m.K, "N": m.N, **rec}
         if m.K not in out["quantize"]:
-            ts = []
-            for _ in range(runs):
-                t0 = time.perf_counter()
-                orc.quantize_rows(X)
-                ts.append(time.perf_counter() - t0)
-            t = float(np.median(ts))
+            t = _median_wall(lambda: orc.quantize_rows(X), runs)
             out["quantize"][m.K] = {"ms": round(t * 1e3, 3),
                                     "GBps": round(quantize_bytes(m.K) / t / 1e9, 4)}
     return out
