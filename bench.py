@@ -85,7 +85,8 @@ def copies_for(nbytes: int) -> int:
 
 class Layer:
     """Packed copies of a workload's matrices (each matrix its own rotation
-    of at least 1 GiB), plus the activation buffers."""
+    of at least 1 GiB, or of MAX_COPIES copies for matrices under 4 MiB),
+    plus the activation buffers."""
 
     def __init__(self, key: str, fused: bool = False):
         import torch
