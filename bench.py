@@ -828,9 +828,11 @@ def timeline_summary(recs: list, split: bool) -> dict:
     return out
 
 
-def timeline_run(key: str, n_live: int, recorded: int = 5) -> dict:
+def timeline_run(key: str, n_live: int, recorded: int = 5, fused: bool = False) -> dict:
     """Per-wave timelines of every matrix's narrow matmul (workspace entry
-    point) from the timeline build: for each matrix, warm-up replays, then
+    point, or with `fused` the fused pre-quantise + matmul, whose records
+    are its matmul workgroups' waves) from the timeline build: for each
+    matrix, warm-up replays, then
     `recorded` times a series of 8 back-to-back launches over the weight
     rotation with recording on; each series leaves the records of its last
     launch."""
@@ -846,8 +848,12 @@ def timeline_run(key: str, n_live: int, recorded: int = 5) -> dict:
         q8.q8_quantize_acts(layer.X[i], 16, m.K, layer.Xq[i])
 
         def launch(c, i=i, m=m):
-            q8.q8_matmul_narrow_ws(layer.weights(i, c), layer.Xq[i], bi, n_live, m.N, m.K,
-                                   layer.Y[i], layer.ws[i])
+            if fused:
+                q8.q8_matmul_narrow_fused(layer.weights(i, c), layer.X[i], 16, layer.Xq[i], bi,
+                                          n_live, m.N, m.K, layer.Y[i], layer.fws[i])
+            else:
+                q8.q8_matmul_narrow_ws(layer.weights(i, c), layer.Xq[i], bi, n_live, m.N, m.K,
+                                       layer.Y[i], layer.ws[i])
         n = layer.launches(i)
         us = float(np.mean(graph_replay_us(launch, n, 3)))
         recs = []
@@ -859,12 +865,13 @@ def timeline_run(key: str, n_live: int, recorded: int = 5) -> dict:
             q8.q8_timeline_set(None, 0)
             torch.cuda.synchronize()
             recs.append(rec.view(-1, q8.Q8_STAMP_WORDS).cpu().numpy().copy())
-        split = q8.q8_matmul_workspace_bytes(m.N, m.K) > 0
+        split = q8.q8_matmul_workspace_bytes(m.N, m.K) > 0  # the same tiling fused
         res[m.name] = dict(timeline_summary(recs, split), K=m.K, N=m.N, n_live=n_live,
                            split=split, timeline_build_us_per_launch=round(us, 3))
         print(f"timeline: {m.name} {m.K}->{m.N}: span {res[m.name]['span_us_median']} us "
               f"(timeline build, graph replays: {us:.2f} us per launch)", flush=True)
-    return {"workload": key, "kernel_source_hash": kernel_source_hash(), "matrices": res}
+    return {"workload": key, "fused": fused, "kernel_source_hash": kernel_source_hash(),
+            "matrices": res}
 
 
 def _counter_rows(path: str, counter: str):
@@ -1087,7 +1094,7 @@ def main(argv=None) -> int:
     import torch
     torch.cuda.set_device(0)
     if args.timeline:
-        res = timeline_run(args.workload, args.n_live)
+        res = timeline_run(args.workload, args.n_live, fused=args.fused)
         text = json.dumps(res, indent=1)
         print(text, flush=True)
         if args.out:

@@ -29,8 +29,9 @@ extern "C" {
 #define Q8_STAMP_WORDS 8 /* uint64 words per wave record */
 
 /* Sets the record buffer of every later matmul launch of this process
- * (q8_matmul_narrow, _ws, _noalloc, _multi, with either engine's dispatch;
- * the fused entry points record nothing).  records: device, 8-byte aligned,
+ * (q8_matmul_narrow, _ws, _noalloc, _multi, and the fused entry points'
+ * matmul workgroups, whose wave index counts from the first matmul
+ * workgroup; the DOT4 engine records nothing).  records: device, 8-byte aligned,
  * caller-owned, at least max_waves * Q8_STAMP_WORDS uint64; null or
  * max_waves = 0 switches recording off.  The launch after this call writes
  * the record of its wave i = blockIdx.x * waves_per_workgroup + wave only if
@@ -41,7 +42,8 @@ extern "C" {
  *
  * Record of one wave of the MFMA matmul (ticks of 10 ns):
  *   [0] the wave starts (after the fused producers' branch)
- *   [1] its first chunk's dot is issued (first weights and slots arrived)
+ *   [1] its first chunk's dot is issued (first weights and slots arrived;
+ *       for the fused entry points, after its wait for the slots)
  *   [2] its last chunk's dot is issued (streaming done)
  *   [3] its workgroup's partial tiles are in LDS (after the barrier)
  *   [4] single-workgroup tree: Y stores issued;

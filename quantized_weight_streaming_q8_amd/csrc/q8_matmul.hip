@@ -1287,8 +1287,11 @@ hipError_t launch_matmul_fused(const uint8_t* Wq, const float* X, int n_rows,
                                hipStream_t st) {
     MmArgs a;
 #ifdef Q8_TIMELINE
-    a.tl = nullptr;  // no timeline of the fused launch
-    a.tl_waves = 0;
+    {  // the matmul workgroups' waves (wave index from the first matmul workgroup)
+        std::lock_guard<std::mutex> lock(g_tl_mu);
+        a.tl = g_tl_buf;
+        a.tl_waves = g_tl_waves;
+    }
 #endif
     a.CT = 1;
     a.wq = Wq;
