@@ -574,11 +574,22 @@ def cpu_detail(key: str, runs: int = 3) -> dict:
 
 # ------------------------------------------------------------- profiles
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments, blank lines and trailing blanks (the
+    kernel sources hold no string literal with a comment marker in it)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line.strip())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the matmul kernel's code (comments and blank lines left out,
+    so that a comment edit does not void the counter summaries)."""
     h = hashlib.sha256()
     for name in ("q8_matmul.hip", "q8_internal.h"):
-        with open(os.path.join(ROOT, "quantized_weight_streaming_q8_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "quantized_weight_streaming_q8_amd", "csrc", name)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -814,6 +825,7 @@ def timeline_summary(recs: list, split: bool) -> dict:
     counts = np.concatenate([c for c, _ in cu_rows])
     ends = np.concatenate([e for _, e in cu_rows])
     out["cus_used"] = int(np.median([c.size for c, _ in cu_rows]))
+    out["cu_last_end_us"] = _pct(ends)  # when each CU's last wave ended, over the CUs
     out["waves_per_cu"] = {int(n): {"cus": int((counts == n).sum() // len(recs)),
                                     "last_end_us_median": round(float(np.median(ends[counts == n])), 3)}
                            for n in np.unique(counts)}

@@ -670,8 +670,10 @@ __device__ inline void combine_splits(const MmArgs& a, int rec, int split, int E
     }
 }
 
-// One workgroup per row block (plain: all S*KW waves) or per (row block,
-// split) (SPLIT: KW waves).  LDS: the wave partials red, fp32, one float4 per
+// One workgroup per row block (plain: all S*KW waves; WHOLE: one wave that
+// takes the S splits in turn) or per (row block, split) (SPLIT: KW waves;
+// with WHOLE, the first n_whole row blocks run as whole workgroups and only
+// the rest as splits).  LDS: the wave partials red, fp32, one float4 per
 // lane and (row group, column tile) of each wave.
 // FUSED: the first P workgroups are producers (see above).
 template <int RG, int CT, int D, bool NTW, bool SPLIT, bool FUSED, bool WHOLE>

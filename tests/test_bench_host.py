@@ -162,3 +162,11 @@ def test_timeline_summary_of_known_records():
     assert p["waves_per_cu"][8]["cus"] == 128 and p["waves_per_cu"][9]["cus"] == 128
     assert p["phases_us"]["y_issue"] == [0.6] * 5 and p["phases_us"]["y_done"] == [0.4] * 5
     assert p["span_us_median"] == 14.46  # latest start 6 + 1440 ticks
+
+
+def test_kernel_hash_ignores_comments_not_code():
+    a = "int f(int x) {\n    return x + 1;  // one more\n}\n"
+    b = "/* block\n   comment */\nint f(int x) {\n\n    // a comment line\n    return x + 1;\n}\n"
+    c = "int f(int x) {\n    return x + 2;\n}\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
