@@ -593,6 +593,23 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def output_digest(layer: Layer, i: int, n_live: int) -> str:
+    """First 16 hex digits of the SHA-256 of matrix i's output bits: its
+    seeded activations pre-quantised, then the workspace matmul on its first
+    weight copy for the workload's seeded batch_index at n_live.  A
+    measurement to compare runs and commits by (a changed summation tree or
+    a regression changes it), not an expected value any test holds."""
+    import torch
+    q8 = layer.q8
+    m = layer.mats[i]
+    bi = layer.batch_index(n_live)
+    Y = torch.empty((n_live, m.N), dtype=torch.float32, device="cuda")
+    q8.q8_quantize_acts(layer.X[i], 16, m.K, layer.Xq[i])
+    q8.q8_matmul_narrow_ws(layer.weights(i, 0), layer.Xq[i], bi, n_live, m.N, m.K, Y, layer.ws[i])
+    torch.cuda.synchronize()
+    return hashlib.sha256(Y.cpu().numpy().tobytes()).hexdigest()[:16]
+
+
 def dominant_matrix(key: str) -> int:
     """Index of a workload's dominant matrix: the largest (gate+up on the
     Qwen3-14B layer)."""
@@ -1188,6 +1205,7 @@ def main(argv=None) -> int:
             "fused_us": round(fu, 2), "fused_GBps": round(fb / fu / 1e3, 1),
             "traffic": measured_traffic(args.workload, m.name, args.n_live, False),
             "weight_copies_rotated": layer.copies[i],
+            "output_sha16": output_digest(layer, i, args.n_live),
         }
     mm_bytes = sum(matmul_bytes(m.N, m.K, args.n_live) for m in mats)
     print(f"# matmuls alone: {sum(kern_us):.1f} us, {mm_bytes / sum(kern_us) / 1e3:.0f} GB/s; "
