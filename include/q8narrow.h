@@ -195,7 +195,7 @@ q8_status q8_matmul_narrow_ws(const void* Wq, const void* Xq,
  * Q8_NOALLOC_SCRATCH_BYTES return Q8_ERR_TOO_LARGE and enqueue nothing
  * (8 MiB holds the split records of up to 1927 row groups of 16 rows, i.e.
  * N <= 30832 for the long rows (K >= 8192) whose row groups are all split;
- * other shapes split at most 255 row groups or none).
+ * other shapes split at most 128 row groups or none).
  *
  * The first call on a device takes the array's device address and enqueues
  * a small kernel on `stream` that zero-fills it; make that first call
