@@ -73,7 +73,7 @@ def _fused(Wq, X, Xq, bi, N, K, ws):
 
 @pytest.mark.parametrize("N,K", [(1, 32), (17, 288), (100, 800), (33, 4128), (40, 17408),
                                  (768, 768), (1000, 5120), (5120, 2080), (7168, 5120),
-                                 (5120, 17408), (17405, 1056), (17981, 2080)])
+                                 (5120, 17408), (17405, 1056), (17981, 2080), (17500, 768)])
 def test_fused_equals_quantize_then_matmul(N, K):
     q8 = _q8()
     rng = np.random.default_rng(N + 3 * K)
