@@ -326,6 +326,88 @@ __device__ inline void load_slot_scales(uint32_t xs[CT], int sc, const uint16_t*
                                                     (int64_t)sc * (4 * kChunkDBytes / 2));
 }
 
+// The same loads as buffer loads, for the multi-tile kernels.  A lane's
+// address is then a buffer descriptor's base (scalar registers) + a
+// wave-uniform offset (a scalar register) + this lane's byte offset (a
+// vector register set once), so an address costs scalar adds only.  Through
+// one per-lane 64-bit pointer each load costs a 64-bit vector add: 30 per
+// super-chunk at four column tiles, where the VALU is the bottleneck.  The
+// one-tile kernels wait on memory, not on the VALU; they keep the global
+// form, for which their ring depths were measured.  Offsets stay below 2^31:
+// a row block's weights are under 1 GiB (K < 2^24, at most 4 row groups),
+// the slot tiles under 2^30 bytes.
+struct Src {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t lane;  // this lane's byte offset
+};
+
+// Operand of the streaming loop: `n` elements from base, this lane's at
+// element lane_el: a per-lane pointer (global form) or a descriptor (BUF).
+// The descriptor: stride 0 (a raw byte range), loads at or past the end
+// read zero, word 3 the gfx9 32-bit data format.
+template <bool BUF, typename T>
+__device__ inline auto operand(const T* base, int64_t n, int lane_el) {
+    if constexpr (BUF) {
+        const int64_t bytes = min(n * (int64_t)sizeof(T), (int64_t)0xffffffffu);
+        return Src{__builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0,
+                                                     (int)(uint32_t)bytes, 0x00020000),
+                   (uint32_t)(lane_el * (int)sizeof(T))};
+    } else {
+        return base + lane_el;
+    }
+}
+
+// aux 2: the non-temporal hint (streamed once, not worth caching)
+template <bool NT>
+__device__ inline v2i64 ld16_v2(const Src& s, int off) {
+    return __builtin_bit_cast(
+        v2i64, __builtin_amdgcn_raw_buffer_load_b128(s.rsrc, (int)s.lane, off, NT ? 2 : 0));
+}
+
+__device__ inline uint32_t ld4(const Src& s, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(s.rsrc, (int)s.lane, off, 0);
+}
+
+// The helpers above for a buffer operand; strides in the same units (bytes
+// for weights and slots, halves for scales), offsets in 32 bits (64-bit
+// ones cost scalar register pairs, and the four-tile kernels then run out of
+// registers).
+template <int RG, int CT, bool NTW>
+__device__ inline void load_chunk_w(Chunk<RG, CT>& ch, int cg, const Src& wq,
+                                    int64_t g_stride_q) {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+        ch.w[rg] = ld16_v2<NTW>(wq, rg * (int)g_stride_q + cg * kChunkBytes);
+}
+
+template <int RG>
+__device__ inline void load_scales(uint32_t ws[RG], int sc, const Src& wd, int64_t g_stride_d) {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+        ws[rg] = ld4(wd, 2 * (rg * (int)g_stride_d + sc * (4 * kChunkDBytes / 2)));
+}
+
+template <int RG, int CT>
+__device__ inline void load_chunk_a(Chunk<RG, CT>& ch, int cg, const Src& xq, int64_t xq_gs) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+        ch.aq[ct] = ld16_v2<false>(xq, ct * (int)xq_gs + cg * kChunkBytes);
+}
+
+template <int RG, int CT, bool NTW>
+__device__ inline void load_chunk(Chunk<RG, CT>& ch, int cg, const Src& wq, int64_t g_stride_q,
+                                  const Src& xq, int64_t xq_gs) {
+    load_chunk_w<RG, CT, NTW>(ch, cg, wq, g_stride_q);
+    load_chunk_a<RG, CT>(ch, cg, xq, xq_gs);
+}
+
+template <int CT>
+__device__ inline void load_slot_scales(uint32_t xs[CT], int sc, const Src& xd, int64_t xd_gs) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+        xs[ct] = ld4(xd, 2 * (ct * (int)xd_gs + sc * (4 * kChunkDBytes / 2)));
+}
+
 // Lane l needs chunk c's dword of its slot l & 15, which lane 16*c + (l & 15)
 // holds: row c of the wave copied to all four 16-lane rows.  A 32-lane swap
 // of the wave with itself gives rows 0101 and 2323, a 16-lane swap of either
@@ -724,12 +806,14 @@ mm_mfma_kernel(MmArgs a) {
     const int64_t gbase = min(g0, a.G - RG);
     const int64_t gq = (int64_t)a.NSC * kScQBytes;              // bytes per row group
     const int64_t gd = (int64_t)a.NSC * 4 * (kChunkDBytes / 2);  // halves per row group
-    const uint8_t* wrow = a.wq + gbase * gq + lane * 16;
     // this lane's scale dword of a super-chunk: row 4*tq + (j & 3) of chunk j >> 2
     const int jl = lane & 15;
-    const uint16_t* wsrow = a.wd + gbase * gd + ((jl >> 2) * kRowsPerGroup + 4 * tq + (jl & 3)) * 2;
-    const uint8_t* xa = a.xq + lane * 16;
-    const uint16_t* xsrow = a.xd + lane * 2;
+    constexpr bool BUF = CT >= 2;
+    const auto wrow = operand<BUF>(a.wq + gbase * gq, (a.G - gbase) * gq, lane * 16);
+    const auto wsrow = operand<BUF>(a.wd + gbase * gd, (a.G - gbase) * gd,
+                                    ((jl >> 2) * kRowsPerGroup + 4 * tq + (jl & 3)) * 2);
+    const auto xa = operand<BUF>(a.xq, a.CT * a.xq_gs, lane * 16);
+    const auto xsrow = operand<BUF>(a.xd, a.CT * a.xd_gs, lane * 2);
     const int gskip = (int)(g0 - gbase);
 
     float acc[RG][CT][4];
@@ -779,6 +863,17 @@ mm_mfma_kernel(MmArgs a) {
         load_slot_scales<CT>(xs_next, sc0, xsrow, a.xd_gs);
 #pragma unroll
         for (int i = 0; i < D; ++i) load_chunk_a<RG, CT>(ring[i], c_lo + i, xa, a.xq_gs);
+    } else if constexpr (BUF) {
+        // in ring order (the barriers keep them so): the loop's first wait is
+        // then for the oldest loads only; left alone, the scheduler may issue
+        // ring[0] last, and the first wait is for all of them
+        load_slot_scales<CT>(xs_next, sc0, xsrow, a.xd_gs);
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, D>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            load_chunk<RG, CT, NTW>(ring[i], c_lo + i, wrow, gq, xa, a.xq_gs);
+            __builtin_amdgcn_sched_barrier(0);
+        });
     } else {
         load_slot_scales<CT>(xs_next, sc0, xsrow, a.xd_gs);
 #pragma unroll
@@ -800,6 +895,11 @@ mm_mfma_kernel(MmArgs a) {
                 constexpr int j = decltype(jc)::value;
                 mfma_chunk<j, RG, CT>(ring[j % D], ws, xb, acc);
                 if constexpr (j == 0) st.mark_once(1);
+                // Two-row-group buffer kernels: nor above the dot (only VALU and
+                // SALU work may cross).  Their ring is near the register limit,
+                // and loads hoisted above the dot need a spare ring slot: the
+                // 4-tile one then spills.
+                if constexpr (BUF && RG >= 2) __builtin_amdgcn_sched_barrier(0x6);
                 if constexpr ((j + D) % 4 == 0) {
                     load_scales<RG>(ws_next, sc + 1, wsrow, gd);
                     load_slot_scales<CT>(xs_next, sc + 1, xsrow, a.xd_gs);
