@@ -799,12 +799,13 @@ def _pct(a) -> list:
 def timeline_summary(recs: list, split: bool) -> dict:
     """Phase durations (us, percentiles over every wave of every recorded
     launch) from timeline-build records (include/q8timeline.h), each launch
-    taken from its own earliest wave start, plus each launch's span and the
-    waves per CU against when each CU's last wave ended."""
+    taken from its own earliest wave start, plus each launch's span, the
+    waves per CU against when each CU's last wave ended, and whether the
+    same CUs end last from launch to launch."""
     ph = {k: [] for k in ("start", "first_chunk", "stream", "reduce", "stream_end", "end")}
     ph.update({k: [] for k in (("publish", "arrive", "combine", "last_tail") if split
                                else ("y_issue", "y_done"))})
-    spans, cu_rows, xcc_rows = [], [], []
+    spans, cu_rows, xcc_rows, cu_keys = [], [], [], []
     for t in recs:
         t = t[t[:, 0] > 0]
         t0 = t[:, 0].min()
@@ -835,6 +836,7 @@ def timeline_summary(recs: list, split: bool) -> dict:
         last_end = np.full(keys.size, -np.inf)
         np.maximum.at(last_end, inv, end)
         cu_rows.append((counts, last_end))
+        cu_keys.append(keys)
     out = {"launches": len(recs), "waves": int((recs[0][:, 0] > 0).sum()),
            "span_us": [round(v, 3) for v in spans], "span_us_median": round(float(np.median(spans)), 3),
            "phases_us": {k: _pct(np.concatenate(v)) for k, v in ph.items()},
@@ -842,6 +844,19 @@ def timeline_summary(recs: list, split: bool) -> dict:
     counts = np.concatenate([c for c, _ in cu_rows])
     ends = np.concatenate([e for _, e in cu_rows])
     out["cus_used"] = int(np.median([c.size for c, _ in cu_rows]))
+    # do the same CUs end last in every launch?  Spearman rank correlation of
+    # the CUs' last-wave end times between every pair of recorded launches
+    # (CUs present in both), median over the pairs: near 1 for CUs that are
+    # slow every time, near 0 for a spread that is new in each launch
+    corr = []
+    for i in range(len(cu_keys)):
+        for j in range(i + 1, len(cu_keys)):
+            _, a, b = np.intersect1d(cu_keys[i], cu_keys[j], return_indices=True)
+            if a.size > 2:
+                ra = np.argsort(np.argsort(cu_rows[i][1][a])).astype(np.float64)
+                rb = np.argsort(np.argsort(cu_rows[j][1][b])).astype(np.float64)
+                corr.append(float(np.corrcoef(ra, rb)[0, 1]))
+    out["cu_end_rank_corr_median"] = round(float(np.median(corr)), 3) if corr else None
     out["cu_last_end_us"] = _pct(ends)  # when each CU's last wave ended, over the CUs
     out["waves_per_cu"] = {int(n): {"cus": int((counts == n).sum() // len(recs)),
                                     "last_end_us_median": round(float(np.median(ends[counts == n])), 3)}

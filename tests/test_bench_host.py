@@ -164,6 +164,29 @@ def test_timeline_summary_of_known_records():
     assert p["span_us_median"] == 14.46  # latest start 6 + 1440 ticks
 
 
+def test_timeline_cu_end_rank_correlation():
+    # one wave per CU; CU c streams for a time set by a per-launch order of the CUs
+    def launch(order):
+        t = _records(256, False)
+        extra = 10 * np.asarray(order, dtype=np.int64)  # ticks of streaming added to CU c
+        for k in (2, 3, 4, 5):
+            t[:256, k] += extra
+        return t
+    same = np.arange(256)
+    rev = same[::-1].copy()
+    perm = np.random.default_rng(5).permutation(256)
+    assert bench.timeline_summary([launch(same), launch(same)], False)["cu_end_rank_corr_median"] == 1.0
+    assert bench.timeline_summary([launch(same), launch(rev)], False)["cu_end_rank_corr_median"] == -1.0
+    from scipy.stats import spearmanr
+    # the record's start offsets (i % 7 ticks) are part of each CU's end time
+    ends_a = np.arange(256) % 7 + 1440 + 10 * same
+    ends_b = np.arange(256) % 7 + 1440 + 10 * perm
+    want = spearmanr(ends_a, ends_b).correlation
+    got = bench.timeline_summary([launch(same), launch(perm)], False)["cu_end_rank_corr_median"]
+    assert abs(got - want) < 1e-3
+    assert bench.timeline_summary([launch(same)], False)["cu_end_rank_corr_median"] is None
+
+
 def test_kernel_hash_ignores_comments_not_code():
     a = "int f(int x) {\n    return x + 1;  // one more\n}\n"
     b = "/* block\n   comment */\nint f(int x) {\n\n    // a comment line\n    return x + 1;\n}\n"
