@@ -104,10 +104,11 @@ __device__ inline int64_t packed_d_index(int64_t row, int64_t blk, int64_t NSC) 
 }
 
 // ------------------------------------------------------------------------
-// q8_0 quantisation of one 8-value segment by a group of 4 lanes that
-// together hold a 32-value block: lanes l, l ^ L, l ^ 2L and l ^ 3L (L = 1:
-// 4 consecutive lanes starting at a multiple of 4; L = 16: lanes 16 apart).
-// All of them must be active.
+// q8_0 quantisation of a 32-value block held by a group of G = 32 / E
+// lanes, E consecutive values each: lane p of the group (p = 0 .. G-1) is
+// lane l0 + p*L, where l0 is a multiple of G*L (L = 1: G consecutive lanes;
+// L = 16: lanes 16 apart).  All of them must be active.  Each lane gets its
+// E codes (little-endian bytes of q[]) and the block's binary16 scale.
 //
 // Blocks the format leaves undefined follow one stated rule each: a block
 // holding a NaN or an infinity stores q = 0 and the binary16 quiet NaN
@@ -115,49 +116,53 @@ __device__ inline int64_t packed_d_index(int64_t row, int64_t blk, int64_t NSC) 
 // absmax/127 rounds to zero (absmax 0, or so small the quotient underflows)
 // is the zero block, q = 0 and d = +0.
 // ------------------------------------------------------------------------
+constexpr uint16_t kNanScale = 0x7E00;  // binary16 quiet NaN
+
+template <int E, int L = 1>
+__device__ inline uint16_t quantize_values(const float v[E], uint32_t q[(E + 3) / 4]) {
+    static_assert(E == 2 || E == 4 || E == 8, "values per lane");
+    static_assert(L == 1 || L == 16, "lane distance of a block's lanes");
+    constexpr int G = 32 / E;
+#pragma unroll
+    for (int i = 0; i < (E + 3) / 4; ++i) q[i] = 0u;
+    // absmax, with a NaN or an infinity counted as +infinity (fmaxf alone
+    // would drop a NaN)
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        const float m = fabsf(v[i]);
+        a = fmaxf(a, m <= __FLT_MAX__ ? m : __builtin_inff());
+    }
+    // absmax of the 32-value block across the group (max is exact in any order)
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) a = fmaxf(a, __shfl_xor(a, m * L, G * L));
+    if (!(a <= __FLT_MAX__)) return kNanScale;  // a NaN or an infinity in the block
+    const float d = a / 127.0f;                    // correctly rounded (no fast-math)
+    if (d == 0.0f) return 0;                       // the zero block, or a scale that underflows
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        float x = roundf(v[i] / d);  // IEEE division, ties away from zero
+        x = fminf(fmaxf(x, -127.0f), 127.0f);
+        const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)x;
+        q[i >> 2] |= b << (8 * (i & 3));
+    }
+    return __builtin_bit_cast(uint16_t, (_Float16)d);  // round to nearest even
+}
+
+// One 8-value segment by a group of 4 lanes (the packer's and the fused
+// producers' mapping).
 struct QuantSeg {
     uint32_t lo, hi;  // 8 int8 values, little-endian
     uint16_t d16;     // binary16 scale of the block
 };
 
-constexpr uint16_t kNanScale = 0x7E00;  // binary16 quiet NaN
-
 template <int L = 1>
 __device__ inline QuantSeg quantize_segment(const float v[8]) {
-    static_assert(L == 1 || L == 16, "lane distance of a block's segments");
-    // absmax, with a NaN or an infinity counted as +infinity (fmaxf alone
-    // would drop a NaN)
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float m = fabsf(v[i]);
-        a = fmaxf(a, m <= __FLT_MAX__ ? m : __builtin_inff());
-    }
-    // absmax of the 32-value block across the 4-lane group (max is exact)
-    a = fmaxf(a, __shfl_xor(a, L, 4 * L));
-    a = fmaxf(a, __shfl_xor(a, 2 * L, 4 * L));
+    uint32_t q[2];
     QuantSeg r;
-    r.lo = r.hi = 0u;
-    if (!(a <= __FLT_MAX__)) {  // a NaN or an infinity in the block
-        r.d16 = kNanScale;
-        return r;
-    }
-    const float d = a / 127.0f;  // correctly rounded (no fast-math)
-    if (d == 0.0f) {             // the zero block, or a scale that underflows
-        r.d16 = 0;
-        return r;
-    }
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float q = roundf(v[i] / d);  // IEEE division, ties away from zero
-        q = fminf(fmaxf(q, -127.0f), 127.0f);
-        const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)q;
-        w[i >> 2] |= b << (8 * (i & 3));
-    }
-    r.lo = w[0];
-    r.hi = w[1];
-    r.d16 = __builtin_bit_cast(uint16_t, (_Float16)d);  // round to nearest even
+    r.d16 = quantize_values<8, L>(v, q);
+    r.lo = q[0];
+    r.hi = q[1];
     return r;
 }
 

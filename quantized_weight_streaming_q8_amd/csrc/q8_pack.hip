@@ -13,12 +13,12 @@
 // layout (16 rows x 2 blocks, 1 KB), lane l holding exactly the 16 bytes it
 // stores at l*16: row l & 15, k-slot l >> 4, 8 values of each of the two
 // blocks.  Every wave's q store is one contiguous 1 KB and its scale store
-// 64 contiguous bytes; a block's 4 segments sit in lanes 16 apart.  The
-// activation pre-quantiser, import and export: one lane per 8-value
-// segment, 4 consecutive lanes per block, consecutive blocks of a row on
-// consecutive lane groups, so a wave reads 2 KB of contiguous fp32 per row
-// (on the 16 short rows of the slots, twice the waves of the packer's
-// mapping and longer contiguous reads: measured faster there).
+// 64 contiguous bytes; a block's 4 segments sit in lanes 16 apart.  Import
+// and export: one lane per 8-value segment, 4 consecutive lanes per block,
+// consecutive blocks of a row on consecutive lane groups.  The activation
+// pre-quantiser: the same order with 2 or 4 values per lane (16 or 8 lanes
+// per block), and one-wave workgroups, which spread the few waves of the
+// 16 short slot rows over the most CUs.
 
 #include "q8_internal.h"
 
@@ -113,20 +113,45 @@ unpack_weights_kernel(const uint8_t* __restrict__ wq, const uint16_t* __restrict
 }
 
 // Activations go to the packed layout of an n_slots-row matrix (row = slot); only
-// rows < n_rows are written.  Any block size (a multiple of 64).
-__global__ void __launch_bounds__(kThreads)
+// rows < n_rows are written.  A block is quantised by 32 / E consecutive
+// lanes, E consecutive values each: the short 16-row input then spreads over
+// many waves, each with few serial divisions, which is what the kernel's
+// latency depends on.  total = n_rows x 8 NSC x 32 / E (whole lane groups).
+template <int E>
+__global__ void __launch_bounds__(64)
 quantize_acts_kernel(const float* __restrict__ X, int64_t K, int64_t KB,
                      int64_t NSC, int64_t total, uint8_t* __restrict__ xq,
                      uint16_t* __restrict__ xd) {
+    constexpr int G = 32 / E;
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (tid >= total) return;
-    const SegIndex ix = seg_index(tid, NSC * kScBlocks);
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (ix.blk < KB) load8(X + ix.row * K + ix.blk * kBlock + ix.seg * 8, v);
-    const QuantSeg r = quantize_segment(v);
-    *reinterpret_cast<uint2*>(xq + packed_q_offset(ix.row, ix.blk, ix.seg, NSC)) =
-        make_uint2(r.lo, r.hi);
-    if (ix.seg == 0) xd[packed_d_index(ix.row, ix.blk, NSC)] = r.d16;
+    if (tid >= total) return;  // whole groups of G lanes: G divides 64 and total
+    const int part = (int)(tid % G);
+    const int64_t b = tid / G;
+    const int64_t blk = b % (NSC * kScBlocks), row = b / (NSC * kScBlocks);
+    float v[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = 0.0f;
+    if (blk < KB) {
+        const float* p = X + row * K + blk * kBlock + part * E;
+        if constexpr (E == 2) {
+            const float2 a = *reinterpret_cast<const float2*>(p);
+            v[0] = a.x; v[1] = a.y;
+        } else if constexpr (E == 4) {
+            const float4 a = *reinterpret_cast<const float4*>(p);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        } else {
+            load8(p, v);
+        }
+    }
+    uint32_t q[(E + 3) / 4];
+    const uint16_t d16 = quantize_values<E>(v, q);
+    // values part*E .. part*E + E - 1 of the block: segment (part*E) / 8, from
+    // byte (part*E) % 8 of it
+    uint8_t* dst = xq + packed_q_offset(row, blk, (part * E) >> 3, NSC) + ((part * E) & 7);
+    if constexpr (E == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)q[0];
+    else if constexpr (E == 4) *reinterpret_cast<uint32_t*>(dst) = q[0];
+    else *reinterpret_cast<uint2*>(dst) = make_uint2(q[0], q[1]);
+    if (part == 0) xd[packed_d_index(row, blk, NSC)] = d16;
 }
 
 inline unsigned grid_for(int64_t total) {
@@ -164,14 +189,21 @@ hipError_t launch_unpack_weights(const uint8_t* Wq, const Shape& s, int8_t* q,
 
 hipError_t launch_quantize_acts(const float* X, int n_rows, const Shape& s,
                                 uint8_t* Xq, int n_slots, hipStream_t st) {
-    const int64_t total = (int64_t)n_rows * s.NSC * kScBlocks * 4;
     uint16_t* xd = reinterpret_cast<uint16_t*>(Xq + (n_slots / kMaxSlots) * s.act_q_bytes);
-    // one-wave workgroups spread the few waves of the 16 slot rows over the
-    // most CUs: 2.16 against 2.36 us at K = 5120 with 256-thread workgroups
-    // (2.33 against 2.54 at K = 17408), same bytes
-    constexpr int kBlock1 = 64;
-    hipLaunchKernelGGL(quantize_acts_kernel, dim3((unsigned)((total + kBlock1 - 1) / kBlock1)),
-                       dim3(kBlock1), 0, st, X, s.K, s.KB, s.NSC, total, Xq, xd);
+    const int64_t blocks = (int64_t)n_rows * s.NSC * kScBlocks;
+    // measured in graph replays (one launch is ~2.1-2.5 us, most of it the
+    // launch itself): 2 values per lane up to about 1000 waves (16 rows of
+    // K <= 8192: 2.10 against 2.18 us with 4 and 2.31 with 8 at K = 5120),
+    // 4 above (16 x 17408: 2.47 against 2.64 with 2 and 2.51 with 8)
+    if (blocks * 16 <= (int64_t)16 * 8192 / 2) {
+        const int64_t total = blocks * 16;
+        hipLaunchKernelGGL(quantize_acts_kernel<2>, dim3((unsigned)((total + 63) / 64)), dim3(64), 0,
+                           st, X, s.K, s.KB, s.NSC, total, Xq, xd);
+    } else {
+        const int64_t total = blocks * 8;
+        hipLaunchKernelGGL(quantize_acts_kernel<4>, dim3((unsigned)((total + 63) / 64)), dim3(64), 0,
+                           st, X, s.K, s.KB, s.NSC, total, Xq, xd);
+    }
     return hipGetLastError();
 }
 
