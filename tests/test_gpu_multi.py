@@ -88,7 +88,8 @@ def test_quantize_acts_n_partial_rows_leave_other_slots():
     assert np.array_equal(q[40:], qb) and np.array_equal(d[40:], db)
 
 
-@pytest.mark.parametrize("N,K", [(17, 288), (100, 800), (33, 4128), (40, 17408), (1000, 5120)])
+# (5, 64): one row group holding 5 rows, one super-chunk of which 2 blocks are real
+@pytest.mark.parametrize("N,K", [(5, 64), (17, 288), (100, 800), (33, 4128), (40, 17408), (1000, 5120)])
 @pytest.mark.parametrize("n_slots", [32, 48, 64])
 def test_multi_matches_oracle(N, K, n_slots):
     rng = np.random.default_rng(N * 7 + K + n_slots)
