@@ -907,8 +907,13 @@ mm_mfma_kernel(MmArgs a) {
                 load_chunk<RG, CT, NTW>(ring[j % D], 4 * sc + j + D, wrow, gq, xa, a.xq_gs);
                 // keep each chunk's loads right after its dot: left alone, the
                 // scheduler sinks all the chunks' loads to the end of the turn,
-                // and every turn then waits a full memory latency
-                __builtin_amdgcn_sched_barrier(0);
+                // and every turn then waits a full memory latency.  The
+                // whole-row four-tile kernel lets MFMA, VALU and SALU work cross
+                // (its next chunk's first MFMAs then issue under this chunk's
+                // last scale arithmetic): gate+up at 64 columns 68.5 -> 66.2 us;
+                // the same for the other multi-tile kernels measured slower
+                if constexpr (WHOLE && CT == 4) __builtin_amdgcn_sched_barrier(0x000E);
+                else __builtin_amdgcn_sched_barrier(0);
             });
         }
         if (!whole || sc >= sc1 - 1) break;
