@@ -1210,7 +1210,8 @@ Tiling choose_tiling(const Shape& s) {
     //  * long rows (K >= 8192) are cut into 4 splits of one wave each, which
     //    the workspace entry point runs as separate single-row-group
     //    workgroups (more of them than there are CUs), 4 chunks in flight
-    //    per wave;
+    //    per wave; when the two-row-group blocks number 205..256 (at least
+    //    80% of the CUs, one each), as 4 wave slices of one workgroup;
     //  * shorter rows are one split.  Below 1024 row groups (16k rows) it is
     //    two row groups per wave and 4 wave slices per row block, 4 chunks
     //    in flight each.  From 1024 row groups on, the weight stream runs
@@ -1238,9 +1239,20 @@ Tiling choose_tiling(const Shape& s) {
     t.seq = false;
     t.split_from = 0;
     if (s.NSC >= 32) {
-        t.splits = 4;
-        t.kw = 1;
-        t.rg_split = 1;
+        const int64_t blocks2 = (s.G + 1) / 2;  // two-row-group row blocks
+        if (s.G >= 2 && 5 * blocks2 >= 4 * kCUs && blocks2 <= kCUs) {
+            // they fill at least 80% of the CUs, one each: the 4 K ranges
+            // are 4 wave slices of one workgroup, summed in LDS (the same
+            // ranges in the same order as 4 splits, so the same bits), and
+            // no workspace: 18432->7168 (224 row blocks) 24.3 against 25.0 us
+            t.splits = 1;
+            t.kw = 4;
+            t.rg_split = 2;
+        } else {
+            t.splits = 4;
+            t.kw = 1;
+            t.rg_split = 1;
+        }
     } else {
         t.splits = 1;
         int64_t kw = 4;

@@ -241,7 +241,11 @@ def test_workspace_sizes(q8):
     # shorter rows are not split
     rec = 256 + 4 * 1024
     assert q8.q8_matmul_workspace_bytes(5120, 17408) == (5120 // 16) * rec
-    assert q8.q8_matmul_workspace_bytes(7168, 18432) == (7168 // 16) * rec
+    # 224 two-row-group blocks fill 88% of the 256 CUs: the K ranges run in one workgroup
+    assert q8.q8_matmul_workspace_bytes(7168, 18432) == 0
+    assert q8.q8_matmul_workspace_bytes(16 * 2 * 204, 18432) == 2 * 204 * rec  # 80% not reached
+    assert q8.q8_matmul_workspace_bytes(16 * 2 * 205, 18432) == 0
+    assert q8.q8_matmul_workspace_bytes(16 * 2 * 257, 18432) == 2 * 257 * rec  # more blocks than CUs
     assert q8.q8_matmul_workspace_bytes(1000, 8224) == 63 * rec
     assert q8.q8_matmul_workspace_bytes(5120, 5120) == 0
     assert q8.q8_matmul_workspace_bytes(151936, 5120) == 0
