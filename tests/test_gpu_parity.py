@@ -249,6 +249,47 @@ def test_matmul_large_ragged_shapes(N, K):
     torch.cuda.empty_cache()
 
 
+# Long rows (K >= 8192) whose two-row-group blocks number 205..256 run their
+# four K ranges as four wave slices of one workgroup; 204 or fewer blocks, or
+# more than 256, run them as four split workgroups.  Both evaluate the same
+# ranges and add them in the same order, so a row's bits do not depend on
+# which side of the boundary its matrix falls: 6555 rows (410 row groups, 205
+# blocks, the last group ragged) against their first 6528 (204 blocks), and
+# 8192 rows (256 blocks) against 8208 (257 blocks).  K = 8224 leaves the last
+# of its 33 super-chunks one block long.
+@pytest.mark.parametrize("N_wg,N_split", [(6555, 6528), (8192, 8208)])
+def test_long_rows_same_bits_either_side_of_the_workgroup_rule(N_wg, N_split):
+    import quantized_weight_streaming_q8_amd as q8
+    K = 8224
+    N = max(N_wg, N_split)
+    assert q8.q8_matmul_workspace_bytes(N_wg, K) == 0
+    assert q8.q8_matmul_workspace_bytes(N_split, K) > 0
+    rng = np.random.default_rng(N_wg)
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    X = _ragged_x(K, seed=K + 3, outliers=True)
+    Xq = gpu_quantize_acts(X)
+    Y = {}
+    for n in (N_wg, N_split):
+        Wq = gpu_pack(np.ascontiguousarray(W[:n]))
+        ws = q8.zeroed_workspace(n, K)
+        rows = sample_rows(n, 96, seed=n)
+        for bi in (rng.permutation(16), np.array([2, 11, 11])):
+            bi = bi.astype(np.int32)
+            Yo, Ao = _oracle_y(W[:n], X, bi, rows)
+            Ym = gpu_matmul(Wq, Xq, bi, n, K, MFMA)
+            ok, worst = within_tau(Ym[:, rows], Yo, Ao)
+            assert ok, (n, K, bi, worst)
+            Yw = gpu_matmul_ws(Wq, Xq, bi, n, K, ws)
+            assert np.array_equal(Ym.view(np.uint32), Yw.view(np.uint32)), (n, bi)
+            Yd = gpu_matmul(Wq, Xq, bi, n, K, DOT4)
+            assert np.array_equal(Ym.view(np.uint32), Yd.view(np.uint32)), (n, bi)
+        Y[n] = gpu_matmul_ws(Wq, Xq, np.arange(16, dtype=np.int32), n, K, ws)
+        del Wq, ws
+    m = min(N_wg, N_split)
+    assert np.array_equal(Y[N_wg][:, :m].view(np.uint32), Y[N_split][:, :m].view(np.uint32))
+    torch.cuda.empty_cache()
+
+
 def test_largest_k():
     """The largest K the boundary takes, 2^24 - 32: 65536 super-chunks, the
     last of them 7 blocks long, split 4 ways across workgroups; N = 17 (a
