@@ -907,13 +907,8 @@ mm_mfma_kernel(MmArgs a) {
                 load_chunk<RG, CT, NTW>(ring[j % D], 4 * sc + j + D, wrow, gq, xa, a.xq_gs);
                 // keep each chunk's loads right after its dot: left alone, the
                 // scheduler sinks all the chunks' loads to the end of the turn,
-                // and every turn then waits a full memory latency.  The
-                // whole-row four-tile kernel lets MFMA, VALU and SALU work cross
-                // (its next chunk's first MFMAs then issue under this chunk's
-                // last scale arithmetic): gate+up at 64 columns 68.5 -> 66.2 us;
-                // the same for the other multi-tile kernels measured slower
-                if constexpr (WHOLE && CT == 4) __builtin_amdgcn_sched_barrier(0x000E);
-                else __builtin_amdgcn_sched_barrier(0);
+                // and every turn then waits a full memory latency
+                __builtin_amdgcn_sched_barrier(0);
             });
         }
         if (!whole || sc >= sc1 - 1) break;
@@ -1368,33 +1363,45 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
     a.recs = split ? static_cast<uint8_t*>(workspace) : nullptr;
     if (t.split_from % rg != 0) return hipErrorInvalidValue;
     a.n_whole = split ? (int)(t.split_from / rg) : t.seq ? a.n_rb : 0;
-    // more than one column tile: a shallower ring keeps the chunk operands
-    // (which grow with the tiles) in registers
+    // More than one column tile: two row groups per wave (one only for a
+    // single row group), so each chunk's activation operand (16 bytes per
+    // lane and column tile) feeds 32 rows, and the S * KW waves of a row
+    // block evaluate the tree's splits and slices side by side, the same
+    // sums as every other execution.  Measured on MI355X, same bits: gate+up
+    // 5120->34816 at 64 columns 66.0 -> 58.1 us against one row group per
+    // whole-row wave, the 152k-row head 263 -> 204.5 us (at 32 columns
+    // 194 -> 149 us).  The ring depth keeps the weights in flight over the
+    // GPU (one KB per row group and chunk) near what each tile width runs
+    // best with: two tiles at most 2 * kInFlightKB at depth 4, 2 or 1; four
+    // tiles at most 2.5 * kInFlightKB at depth 4, else 2 (at depth 1 a
+    // wave's four tiles of arithmetic stall on every chunk); three tiles
+    // hold 2 chunks in registers.
     if (a.CT > 1) {
-        // measured on MI355X: many row blocks (large N) run best with one
-        // row group and two chunks in flight per wave (more waves), few with
-        // two row groups and four chunks
-        const bool wide = (s.G + 1) / 2 >= 512 || rg == 1;
-        a.n_rb = (int)(wide ? s.G : (s.G + 1) / 2);
-        // a tree of S splits runs as one wave per split (S waves per row
-        // block, the same sums) unless that puts well over kInFlightKB of
-        // weights in flight (2 chunks of 1 KB per wave): measured, 7168->18432
-        // at 32 columns 34.4 against 44.0 us with whole-row waves, gate+up
-        // 41.2 whole against 46.2 us
-        const bool split_waves = 2 * (int64_t)a.n_rb * t.splits <= 3 * kInFlightKB / 2;
-        a.n_whole = (t.seq && wide && !split_waves) ? a.n_rb : 0;
-#define Q8_LAUNCH_CT(C, D2)                                                     \
-    case C:                                                                     \
-        return wide ? (a.n_whole > 0 ? launch_mfma<1, C, 2, true, false, false, true>(a, st) \
-                                     : launch_mfma<1, C, 2, true, false>(a, st))            \
-                    : launch_mfma<2, C, D2, true, false>(a, st);
+        const int rg2 = s.G >= 2 ? 2 : 1;
+        a.n_rb = (int)((s.G + rg2 - 1) / rg2);
+        a.n_whole = 0;
+        const int64_t kb = (int64_t)a.n_rb * t.splits * t.kw * rg2;  // KB per chunk of every wave
+        const int d2 = 4 * kb <= 2 * kInFlightKB ? 4 : 2 * kb <= 2 * kInFlightKB ? 2 : 1;
+        const int d4 = 8 * kb <= 5 * kInFlightKB ? 4 : 2;
+        if (rg2 == 1) {
+            switch (a.CT) {
+                case 2: return launch_mfma<1, 2, 2, true, false>(a, st);
+                case 3: return launch_mfma<1, 3, 2, true, false>(a, st);
+                case 4: return launch_mfma<1, 4, 2, true, false>(a, st);
+                default: return hipErrorInvalidValue;
+            }
+        }
         switch (a.CT) {
-            Q8_LAUNCH_CT(2, 4)
-            Q8_LAUNCH_CT(3, 2)  // three tiles and four chunks do not fit the registers
-            Q8_LAUNCH_CT(4, 4)
+            case 2:
+                return d2 == 4 ? launch_mfma<2, 2, 4, true, false>(a, st)
+                     : d2 == 2 ? launch_mfma<2, 2, 2, true, false>(a, st)
+                               : launch_mfma<2, 2, 1, true, false>(a, st);
+            case 3: return launch_mfma<2, 3, 2, true, false>(a, st);
+            case 4:
+                return d4 == 4 ? launch_mfma<2, 4, 4, true, false>(a, st)
+                               : launch_mfma<2, 4, 2, true, false>(a, st);
             default: return hipErrorInvalidValue;
         }
-#undef Q8_LAUNCH_CT
     }
     return launch_ct1<false>(a, rg, split, t.ring, t.nt_weights, st);
 }
