@@ -1222,7 +1222,7 @@ Tiling choose_tiling(const Shape& s) {
     //    groups are not a multiple of the 256 CUs: with gate+up's 2176, 128
     //    CUs stream 9 row groups and 128 stream 8, and the kernel lasts as
     //    long as the 9.  Then the tree has S = min(4, 256 / r, NSC) splits
-    //    (r = G mod 256, S >= 2) and the split execution runs the first
+    //    (r = G mod 256, S >= 2; 4 for r = 128) and the split execution runs the first
     //    G - r row groups as one wave each that evaluates the splits in turn
     //    and only the last r as S one-split workgroups each: at most one
     //    piece per CU, dispatched after the whole rows.  Every other
@@ -1257,7 +1257,13 @@ Tiling choose_tiling(const Shape& s) {
                 t.rg = 1;
                 t.ring = 3 * s.G <= kInFlightKB ? 4 : 3 * s.G <= 2 * kInFlightKB ? 2 : 1;
                 const int64_t r = s.G % kCUs;
-                const int64_t st = r == 0 ? 1 : std::min<int64_t>({4, kCUs / r, s.NSC});
+                int64_t st = r == 0 ? 1 : std::min<int64_t>({4, kCUs / r, s.NSC});
+                // r = 128: 4 splits put exactly two quarter-row pieces on
+                // every CU, as even as one half-row piece, and give the
+                // multi-column launches (one wave per split) twice the
+                // waves: 7168->18432 at 64 columns 51.5 -> 44.7 us, the
+                // one-column kernels unchanged
+                if (2 * r == kCUs && s.NSC >= 4) st = 4;
                 if (st >= 2) {
                     t.splits = (int)st;
                     t.seq = true;
@@ -1372,7 +1378,9 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
     // whole-row wave, the 152k-row head 263 -> 204.5 us (at 32 columns
     // 194 -> 149 us).  The ring depth keeps the weights in flight over the
     // GPU (one KB per row group and chunk) near what each tile width runs
-    // best with: two tiles at most 2 * kInFlightKB at depth 4, 2 or 1; four
+    // best with: two tiles at most 2 * kInFlightKB at depth 4, 2 or 1 (4
+    // whenever a row is cut into 4 or more wave slices: short waves need the
+    // depth, gate+up at 32 columns 40.4 us at 4, 41.7 at 1); four
     // tiles at most 2.5 * kInFlightKB at depth 4, else 2 (at depth 1 a
     // wave's four tiles of arithmetic stall on every chunk); three tiles
     // hold 2 chunks in registers.
@@ -1381,7 +1389,8 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
         a.n_rb = (int)((s.G + rg2 - 1) / rg2);
         a.n_whole = 0;
         const int64_t kb = (int64_t)a.n_rb * t.splits * t.kw * rg2;  // KB per chunk of every wave
-        const int d2 = 4 * kb <= 2 * kInFlightKB ? 4 : 2 * kb <= 2 * kInFlightKB ? 2 : 1;
+        const int d2 = (4 * kb <= 2 * kInFlightKB || t.splits * t.kw >= 4) ? 4
+                     : 2 * kb <= 2 * kInFlightKB ? 2 : 1;
         const int d4 = 8 * kb <= 5 * kInFlightKB ? 4 : 2;
         if (rg2 == 1) {
             switch (a.CT) {

@@ -108,13 +108,14 @@ def test_multi_matches_oracle(N, K, n_slots):
         assert ok, (N, K, n_slots, bi[:8], worst)
 
 
-# (17405, 1056): 1088 row groups, a 4-split tree evaluated one wave per row
-# group; (17981, 2080): 1124 row groups, a 2-split tree that the multi-column
-# launch runs as one wave per split; (17500, 768): 3 splits as 3 waves;
-# (6555, 8224): 205 two-row-group blocks of long rows, four K ranges in one
-# workgroup
+# The multi-column launch runs a row block's splits as waves of one workgroup,
+# where the 16-slot kernel evaluates them in one whole-row wave or as split
+# workgroups: (17405, 1056) 1088 row groups, 4 splits; (17981, 2080) 1124 row
+# groups, 2 splits; (17500, 768) 3 splits; (18429, 1056) 1152 row groups
+# (r = 128), 4 splits; (6555, 8224) 205 two-row-group blocks of long rows,
+# four K ranges in one workgroup
 @pytest.mark.parametrize("N,K", [(100, 800), (40, 17408), (2304, 5120), (17405, 1056),
-                                 (17981, 2080), (17500, 768), (6555, 8224)])
+                                 (17981, 2080), (17500, 768), (6555, 8224), (18429, 1056)])
 def test_multi_columns_equal_the_16_slot_kernel(N, K):
     """Slot 16c + s of a 64-slot buffer gives the bits of slot s of a 16-slot
     buffer holding the same rows; n_slots = 16 is the 16-slot kernel itself."""

@@ -214,14 +214,15 @@ def test_matmul_ragged_shapes(N, K):
 # not a multiple of 16 and K leaves the last super-chunk partly empty.  For
 # G mod 256 = r in 1..128 the tree has min(4, 256 / r, NSC) splits, and the
 # workspace entry point runs only the last r row groups as split workgroups:
-# r = 1 (4 splits), 100 (2 splits), 64 (4 splits); 209 and 185 are not split.
+# r = 1 (4 splits), 100 (2 splits), 64 (4 splits), 128 (4 splits, two pieces
+# per CU); 209 and 185 are not split.
 # r = 70 gives 3 splits (K = 1312: folds at super-chunks 2 and 4 of 6; K = 768:
 # at 1 and 2 of 3, the second on the last super-chunk); r = 100 with K = 512
 # folds on the last of its 2 super-chunks.  18992 x 5120 is one of eight
 # column shards of the 151936-row head (1187 row groups, r = 163: not split).
 @pytest.mark.parametrize("N,K", [(16391, 4128), (32005, 800), (48003, 1056), (72009, 800),
                                  (17981, 2080), (17405, 1056), (17500, 1312), (17500, 768),
-                                 (17981, 512), (18992, 5120)])
+                                 (17981, 512), (18992, 5120), (18429, 1056)])
 def test_matmul_large_ragged_shapes(N, K):
     rng = np.random.default_rng(N - K)
     W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
