@@ -134,6 +134,39 @@ def test_multi_columns_equal_the_16_slot_kernel(N, K):
         assert np.array_equal(Y16.view(np.uint32), Y1.view(np.uint32)), c
 
 
+# Launch shapes of the multi-column kernels (two row groups per wave; ring
+# depth from the weights in flight): (17981, 2080) 1124 row groups with 2
+# splits runs two tiles at depth 2 and four at depth 4; (72003, 256) 4501 row
+# groups in one split, two tiles at depth 1 and four at depth 2; (18429, 1056)
+# 1152 row groups with 4 splits, two tiles at depth 4 and four at depth 2;
+# three tiles run at depth 2 everywhere.
+@pytest.mark.parametrize("N,K", [(17981, 2080), (72003, 256), (18429, 1056)])
+def test_multi_widths_equal_the_16_slot_kernel(N, K):
+    """At 32, 48 and 64 slots every 16-slot group of columns gives the bits
+    of the 16-slot kernel on the same rows, and sampled rows of the 64-slot
+    result match the oracle."""
+    rng = np.random.default_rng(N - K)
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    X = _x(64, K, seed=K + 11)
+    Wq = gpu_pack(W)
+    Y16 = []
+    for c in range(4):
+        Xq16 = _quantize(np.ascontiguousarray(X[16 * c:16 * c + 16]), 16)
+        Y16.append(gpu_matmul(Wq, Xq16, np.arange(16, dtype=np.int32), N, K))
+    for n in (32, 48, 64):
+        Xq = _quantize(np.ascontiguousarray(X[:n]), n)
+        Y = _multi(Wq, Xq, n, np.arange(n, dtype=np.int32), N, K)
+        for c in range(n // 16):
+            assert np.array_equal(Y[16 * c:16 * c + 16].view(np.uint32), Y16[c].view(np.uint32)), (n, c)
+    rows = sample_rows(N, 64, seed=N)
+    qw, dw = oracle.quantize_rows(W[rows])
+    qx, dx = oracle.quantize_rows(X)
+    bi = rng.permutation(64).astype(np.int32)
+    Yo, Ao = oracle.matmul(qw, dw, qx, dx, bi)
+    ok, worst = within_tau(Y[bi][:, rows], Yo, Ao)
+    assert ok, worst
+
+
 def test_multi_columns_equal_single_token_calls():
     N, K, n_slots = 2304, 5120, 64
     rng = np.random.default_rng(9)
