@@ -154,7 +154,10 @@ size_t q8_matmul_workspace_bytes(int64_t N, int64_t K);
 
 /* q8_matmul_narrow, executed with the K splits of row blocks spread over
  * separate workgroups: every row block for long rows (K >= 8192), which
- * balances small-N shapes over the whole GPU; for 1024..4400 row groups of
+ * balances small-N shapes over the whole GPU (except when the row blocks of
+ * two row groups of 16 rows number 205..256: those shapes fill 80-100% of
+ * the CUs with one workgroup each, which adds its 4 K ranges in LDS, and
+ * need no workspace); for 1024..4400 row groups of
  * 16 rows that are not a multiple of the GPU's 256 CUs, only the last
  * (row groups mod 256) row blocks, so that every CU streams the same bytes.
  * The splits meet through `workspace` (device memory, 256-byte aligned, at
