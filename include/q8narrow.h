@@ -181,6 +181,40 @@ q8_status q8_matmul_narrow_ws(const void* Wq, const void* Xq,
                               int64_t N, int64_t K, float* Y, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------- launch plan */
+
+/* The MFMA engine's launch for an N x K matrix, as the matmul entry points
+ * enqueue it: q8_matmul_narrow (with_workspace = 0, n_slots = 16),
+ * q8_matmul_narrow_ws and q8_matmul_narrow_noalloc (with_workspace = 1,
+ * n_slots = 16), q8_matmul_multi (with_workspace = 0, n_slots 32, 48 or 64).
+ * Everything here follows from (N, K, n_slots) alone, never from the live
+ * batch, which is what keeps a column's bits independent of it.  The fields
+ * name the fixed summation tree (a wave adds its blocks in order, the
+ * slices of a split are added in order, then the splits in order) and how
+ * the launch evaluates it.
+ * The fused entry point launches the with_workspace = 1 plan plus its
+ * producer workgroups, at 4 chunks in flight.  Host only: no device call. */
+typedef struct {
+    int32_t row_groups_per_wave;   /* row groups of 16 rows each wave streams */
+    int32_t column_tiles;          /* n_slots / 16 */
+    int32_t chunks_in_flight;      /* weight chunks (1 KB per row group) per wave */
+    int32_t k_splits;              /* splits of K (the tree's level 2) */
+    int32_t slices_per_split;      /* wave slices of a split (level 1) */
+    int32_t split_workgroups;      /* 1: the splits of some row blocks run as
+                                      separate workgroups meeting in the workspace */
+    int32_t whole_row_workgroups;  /* leading workgroups of one wave that
+                                      evaluates every split of its row block in turn */
+    int32_t waves_per_workgroup;   /* of 64 lanes */
+    int64_t workgroups;
+    int64_t lds_bytes;             /* dynamic LDS per workgroup */
+} q8_launch_info;
+
+/* Fills *info.  Q8_ERR_INVALID_ARG for a null info, an invalid shape, an
+ * n_slots other than 16, 32, 48 or 64, or with_workspace other than 0 or
+ * 1 (1 only with n_slots = 16); else Q8_OK. */
+q8_status q8_matmul_launch_info(int64_t N, int64_t K, int n_slots, int with_workspace,
+                                q8_launch_info* info);
+
 /* ----------------------------------------------- no-allocation variant */
 
 /* Bytes of the device array behind q8_matmul_narrow_noalloc (8 MiB). */

@@ -56,6 +56,7 @@ _SIGNATURES = {
     "q8_matmul_narrow": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp], _i32),
     "q8_matmul_narrow_path": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp, _i32], _i32),
     "q8_matmul_workspace_bytes": ([_i64, _i64], ctypes.c_size_t),
+    "q8_matmul_launch_info": ([_i64, _i64, _i32, _i32, _vp], _i32),
     "q8_matmul_narrow_ws": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp], _i32),
     "q8_matmul_narrow_noalloc": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp], _i32),
     "q8_matmul_fused_workspace_bytes": ([_i64, _i64], ctypes.c_size_t),
@@ -238,6 +239,23 @@ def q8_matmul_narrow_path(Wq, Xq, batch_index, n_live: int, N: int, K: int, Y,
 
 def q8_matmul_workspace_bytes(N: int, K: int) -> int:
     return int(_lib.q8_matmul_workspace_bytes(N, K))
+
+
+class _LaunchInfo(ctypes.Structure):
+    _fields_ = [("row_groups_per_wave", ctypes.c_int32), ("column_tiles", ctypes.c_int32),
+                ("chunks_in_flight", ctypes.c_int32), ("k_splits", ctypes.c_int32),
+                ("slices_per_split", ctypes.c_int32), ("split_workgroups", ctypes.c_int32),
+                ("whole_row_workgroups", ctypes.c_int32), ("waves_per_workgroup", ctypes.c_int32),
+                ("workgroups", ctypes.c_int64), ("lds_bytes", ctypes.c_int64)]
+
+
+def q8_matmul_launch_info(N: int, K: int, n_slots: int = Q8_MAX_SLOTS,
+                          with_workspace: bool = False) -> dict:
+    """The MFMA engine's launch for an N x K matrix (host only)."""
+    info = _LaunchInfo()
+    _check(_lib.q8_matmul_launch_info(N, K, n_slots, int(with_workspace), ctypes.byref(info)),
+           "q8_matmul_launch_info")
+    return {name: int(getattr(info, name)) for name, _ in _LaunchInfo._fields_}
 
 
 def _ws_bytes(workspace, workspace_bytes):

@@ -162,6 +162,29 @@ size_t q8_matmul_workspace_bytes(int64_t N, int64_t K) {
     return q8::workspace_bytes(s, q8::choose_tiling(s));
 }
 
+q8_status q8_matmul_launch_info(int64_t N, int64_t K, int n_slots, int with_workspace,
+                                q8_launch_info* info) {
+    if (info == nullptr || !valid_shape(N, K)) return Q8_ERR_INVALID_ARG;
+    if (with_workspace != 0 && (with_workspace != 1 || n_slots != Q8_MAX_SLOTS))
+        return Q8_ERR_INVALID_ARG;
+    const q8::Shape s = q8::make_shape(N, K);
+    const q8::Tiling t = q8::choose_tiling(s);
+    q8::MmPlan p;
+    if (!q8::plan_matmul(s, t, n_slots, with_workspace == 1 && q8::workspace_bytes(s, t) > 0, p))
+        return Q8_ERR_INVALID_ARG;
+    info->row_groups_per_wave = p.rg;
+    info->column_tiles = p.ct;
+    info->chunks_in_flight = p.ring;
+    info->k_splits = p.splits;
+    info->slices_per_split = p.kw;
+    info->split_workgroups = p.split ? 1 : 0;
+    info->whole_row_workgroups = p.n_whole;
+    info->waves_per_workgroup = p.waves;
+    info->workgroups = p.workgroups;
+    info->lds_bytes = (int64_t)p.lds_bytes;
+    return Q8_OK;
+}
+
 q8_status q8_matmul_narrow_ws(const void* Wq, const void* Xq,
                               const int32_t* batch_index, int n_live, int64_t N,
                               int64_t K, float* Y, void* workspace,

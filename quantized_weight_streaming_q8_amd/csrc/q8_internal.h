@@ -203,6 +203,26 @@ hipError_t launch_rope_multi(float* Y, int n_rows, int64_t row_stride, const int
                              int n_heads, int head_dim, double base, hipStream_t st);
 // Workspace a split execution needs (0: the shape is not split).
 size_t workspace_bytes(const Shape& s, const Tiling& t);
+
+// The MFMA engine's launch for one call, decided from the shape, the tiling,
+// the slot buffer's width and whether the splits run through a workspace
+// (the fused entry point adds its producer workgroups and keeps 4 chunks in
+// flight).
+struct MmPlan {
+    int rg;              // row groups per wave
+    int ct;              // 16-slot column tiles
+    int ring;            // chunks in flight per wave
+    int splits, kw;      // the tree: splits (level 2), wave slices per split (level 1)
+    bool split;          // splits as separate workgroups, meeting in the workspace
+    int n_rb;            // row blocks of rg row groups
+    int n_whole;         // leading row blocks run by one wave that takes every split in turn
+    int waves;           // waves per workgroup
+    int64_t workgroups;
+    size_t lds_bytes;    // dynamic LDS per workgroup
+};
+// false: the slot width or the tiling cannot be launched.
+bool plan_matmul(const Shape& s, const Tiling& t, int n_slots, bool with_workspace,
+                 MmPlan& p);
 // Workspace of the fused pre-quantise + matmul: 64 KB of counters and flags
 // (16 pages of 4 KB), then workspace_bytes().  The uint32 at byte
 // kFusedTimeoutsOffset counts the matmul workgroups whose bounded wait ran

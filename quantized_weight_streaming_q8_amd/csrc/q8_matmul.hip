@@ -1315,6 +1315,52 @@ size_t workspace_bytes(const Shape& s, const Tiling& t) {
     return (size_t)(n_rb * record_bytes(t.splits, rg * 256));
 }
 
+bool plan_matmul(const Shape& s, const Tiling& t, int n_slots, bool with_workspace,
+                 MmPlan& p) {
+    p.ct = n_slots / kMaxSlots;
+    if (p.ct < 1 || p.ct * kMaxSlots != n_slots || n_slots > kMaxColumns) return false;
+    if (t.splits * t.kw > s.NSC) return false;
+    p.splits = t.splits;
+    p.kw = t.kw;
+    p.split = with_workspace && t.splits > 1;
+    if (p.split && p.ct != 1) return false;
+    if (p.ct == 1) {
+        p.rg = launch_rg(s, t, p.split);
+        p.ring = t.ring;
+        if (t.split_from % p.rg != 0) return false;
+        p.n_rb = (int)((s.G + p.rg - 1) / p.rg);
+        p.n_whole = p.split ? (int)(t.split_from / p.rg) : t.seq ? p.n_rb : 0;
+    } else {
+        // More than one column tile: two row groups per wave (one only for a
+        // single row group), so each chunk's activation operand (16 bytes per
+        // lane and column tile) feeds 32 rows, and the S * KW waves of a row
+        // block evaluate the tree's splits and slices side by side, the same
+        // sums as every other execution.  Measured on MI355X, same bits: gate+up
+        // 5120->34816 at 64 columns 66.0 -> 58.1 us against one row group per
+        // whole-row wave, the 152k-row head 263 -> 204.5 us (at 32 columns
+        // 194 -> 149 us).  The ring depth keeps the weights in flight over the
+        // GPU (one KB per row group and chunk) near what each tile width runs
+        // best with: two tiles at most 2 * kInFlightKB at depth 4, 2 or 1 (4
+        // whenever a row is cut into 4 or more wave slices: short waves need the
+        // depth, gate+up at 32 columns 40.4 us at 4, 41.7 at 1); four
+        // tiles at most 2.5 * kInFlightKB at depth 4, else 2 (at depth 1 a
+        // wave's four tiles of arithmetic stall on every chunk); three tiles
+        // hold 2 chunks in registers.
+        p.rg = s.G >= 2 ? 2 : 1;
+        p.n_rb = (int)((s.G + p.rg - 1) / p.rg);
+        p.n_whole = 0;
+        const int64_t kb = (int64_t)p.n_rb * t.splits * t.kw * p.rg;  // KB per chunk of every wave
+        const int d2 = (4 * kb <= 2 * kInFlightKB || t.splits * t.kw >= 4) ? 4
+                     : 2 * kb <= 2 * kInFlightKB ? 2 : 1;
+        const int d4 = 8 * kb <= 5 * kInFlightKB ? 4 : 2;
+        p.ring = p.rg == 1 || p.ct == 3 ? 2 : p.ct == 2 ? d2 : d4;
+    }
+    p.waves = (p.split || p.n_whole > 0) ? t.kw : t.splits * t.kw;
+    p.workgroups = p.split ? p.n_whole + (int64_t)(p.n_rb - p.n_whole) * t.splits : p.n_rb;
+    p.lds_bytes = (size_t)p.waves * p.rg * p.ct * 256 * sizeof(float);
+    return true;
+}
+
 #ifdef Q8_TIMELINE
 namespace {
 std::mutex g_tl_mu;
@@ -1362,57 +1408,31 @@ hipError_t launch_matmul(Engine e, const uint8_t* Wq, const uint8_t* Xq,
     if (a.S * a.KW > a.NSC) return hipErrorInvalidValue;
     a.n_whole = 0;
     if (e == Engine::kDot4) return a.CT == 1 ? launch_dot4(a, st) : hipErrorInvalidValue;
-    const bool split = workspace != nullptr && t.splits > 1;
-    if (split && a.CT != 1) return hipErrorInvalidValue;
-    const int rg = launch_rg(s, t, split);
-    a.n_rb = (int)((s.G + rg - 1) / rg);
-    a.recs = split ? static_cast<uint8_t*>(workspace) : nullptr;
-    if (t.split_from % rg != 0) return hipErrorInvalidValue;
-    a.n_whole = split ? (int)(t.split_from / rg) : t.seq ? a.n_rb : 0;
-    // More than one column tile: two row groups per wave (one only for a
-    // single row group), so each chunk's activation operand (16 bytes per
-    // lane and column tile) feeds 32 rows, and the S * KW waves of a row
-    // block evaluate the tree's splits and slices side by side, the same
-    // sums as every other execution.  Measured on MI355X, same bits: gate+up
-    // 5120->34816 at 64 columns 66.0 -> 58.1 us against one row group per
-    // whole-row wave, the 152k-row head 263 -> 204.5 us (at 32 columns
-    // 194 -> 149 us).  The ring depth keeps the weights in flight over the
-    // GPU (one KB per row group and chunk) near what each tile width runs
-    // best with: two tiles at most 2 * kInFlightKB at depth 4, 2 or 1 (4
-    // whenever a row is cut into 4 or more wave slices: short waves need the
-    // depth, gate+up at 32 columns 40.4 us at 4, 41.7 at 1); four
-    // tiles at most 2.5 * kInFlightKB at depth 4, else 2 (at depth 1 a
-    // wave's four tiles of arithmetic stall on every chunk); three tiles
-    // hold 2 chunks in registers.
-    if (a.CT > 1) {
-        const int rg2 = s.G >= 2 ? 2 : 1;
-        a.n_rb = (int)((s.G + rg2 - 1) / rg2);
-        a.n_whole = 0;
-        const int64_t kb = (int64_t)a.n_rb * t.splits * t.kw * rg2;  // KB per chunk of every wave
-        const int d2 = (4 * kb <= 2 * kInFlightKB || t.splits * t.kw >= 4) ? 4
-                     : 2 * kb <= 2 * kInFlightKB ? 2 : 1;
-        const int d4 = 8 * kb <= 5 * kInFlightKB ? 4 : 2;
-        if (rg2 == 1) {
-            switch (a.CT) {
-                case 2: return launch_mfma<1, 2, 2, true, false>(a, st);
-                case 3: return launch_mfma<1, 3, 2, true, false>(a, st);
-                case 4: return launch_mfma<1, 4, 2, true, false>(a, st);
-                default: return hipErrorInvalidValue;
-            }
-        }
-        switch (a.CT) {
-            case 2:
-                return d2 == 4 ? launch_mfma<2, 2, 4, true, false>(a, st)
-                     : d2 == 2 ? launch_mfma<2, 2, 2, true, false>(a, st)
-                               : launch_mfma<2, 2, 1, true, false>(a, st);
-            case 3: return launch_mfma<2, 3, 2, true, false>(a, st);
-            case 4:
-                return d4 == 4 ? launch_mfma<2, 4, 4, true, false>(a, st)
-                               : launch_mfma<2, 4, 2, true, false>(a, st);
+    MmPlan p;
+    if (!plan_matmul(s, t, n_slots, workspace != nullptr, p)) return hipErrorInvalidValue;
+    a.n_rb = p.n_rb;
+    a.n_whole = p.n_whole;
+    a.recs = p.split ? static_cast<uint8_t*>(workspace) : nullptr;
+    if (p.ct == 1) return launch_ct1<false>(a, p.rg, p.split, p.ring, t.nt_weights, st);
+    if (p.rg == 1) {
+        switch (p.ct) {
+            case 2: return launch_mfma<1, 2, 2, true, false>(a, st);
+            case 3: return launch_mfma<1, 3, 2, true, false>(a, st);
+            case 4: return launch_mfma<1, 4, 2, true, false>(a, st);
             default: return hipErrorInvalidValue;
         }
     }
-    return launch_ct1<false>(a, rg, split, t.ring, t.nt_weights, st);
+    switch (p.ct) {
+        case 2:
+            return p.ring == 4 ? launch_mfma<2, 2, 4, true, false>(a, st)
+                 : p.ring == 2 ? launch_mfma<2, 2, 2, true, false>(a, st)
+                               : launch_mfma<2, 2, 1, true, false>(a, st);
+        case 3: return launch_mfma<2, 3, 2, true, false>(a, st);
+        case 4:
+            return p.ring == 4 ? launch_mfma<2, 4, 4, true, false>(a, st)
+                               : launch_mfma<2, 4, 2, true, false>(a, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_matmul_fused(const uint8_t* Wq, const float* X, int n_rows,

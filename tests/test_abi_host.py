@@ -29,7 +29,7 @@ def test_header_declares_the_abi():
     names = header_functions()
     for core in ("q8_pack_weights", "q8_quantize_acts", "q8_matmul_narrow"):
         assert core in names
-    assert len(names) == 21, names
+    assert len(names) == 22, names
 
 
 def test_every_declared_symbol_is_exported(q8):
@@ -259,6 +259,81 @@ def test_workspace_sizes(q8):
     assert q8.q8_matmul_workspace_bytes(16391, 5120) == 1 * rec     # 1025: one ragged row group
     assert q8.q8_matmul_workspace_bytes(32768, 5120) == 0           # 2048 = 8*256
     assert q8.q8_matmul_workspace_bytes(16 * (1024 + 129), 5120) == 0  # r = 129: one split only
+
+
+# (N, K, n_slots, with_workspace) -> row groups per wave, column tiles,
+# chunks in flight, K splits, slices per split, split workgroups, whole-row
+# workgroups, waves per workgroup, workgroups.  The Qwen3-14B layer and head,
+# the large dense pair, and a one-row-group matrix; their grids (workgroups x
+# waves x 64 lanes) are the ones the kernel traces record.
+LAUNCH_PLANS = {
+    (7168, 5120, 16, 0): (2, 1, 4, 1, 4, 0, 0, 4, 224),      # QKV: 4 K slices in one workgroup
+    (5120, 5120, 16, 0): (2, 1, 4, 1, 4, 0, 0, 4, 160),      # O
+    (34816, 5120, 16, 0): (1, 1, 2, 4, 1, 0, 2176, 1, 2176),  # gate+up: whole rows, 4 splits in turn
+    (34816, 5120, 16, 1): (1, 1, 2, 4, 1, 1, 2048, 1, 2560),  # ... the last 128 as 4 pieces each
+    (5120, 17408, 16, 0): (2, 1, 4, 4, 1, 0, 0, 4, 160),     # down: 4 splits as waves
+    (5120, 17408, 16, 1): (1, 1, 4, 4, 1, 1, 0, 1, 1280),    # ... as one-wave workgroups
+    (151936, 5120, 16, 0): (2, 1, 1, 1, 1, 0, 0, 1, 4748),   # head: two row groups, one chunk
+    (18432, 7168, 16, 1): (1, 1, 4, 4, 1, 1, 1024, 1, 1536),  # 7168->18432
+    (7168, 18432, 16, 1): (2, 1, 4, 1, 4, 0, 0, 4, 224),     # 18432->7168: 205..256 blocks, no split
+    (34816, 5120, 32, 0): (2, 2, 4, 4, 1, 0, 0, 4, 1088),    # multi-column: two row groups per wave
+    (34816, 5120, 48, 0): (2, 3, 2, 4, 1, 0, 0, 4, 1088),
+    (34816, 5120, 64, 0): (2, 4, 2, 4, 1, 0, 0, 4, 1088),
+    (7168, 5120, 64, 0): (2, 4, 4, 1, 4, 0, 0, 4, 224),
+    (151936, 5120, 32, 0): (2, 2, 1, 1, 1, 0, 0, 1, 4748),
+    (151936, 5120, 64, 0): (2, 4, 2, 1, 1, 0, 0, 1, 4748),
+    (5, 64, 64, 0): (1, 4, 2, 1, 1, 0, 0, 1, 1),              # one row group
+}
+_PLAN_KEYS = ("row_groups_per_wave", "column_tiles", "chunks_in_flight", "k_splits",
+              "slices_per_split", "split_workgroups", "whole_row_workgroups",
+              "waves_per_workgroup", "workgroups")
+
+
+@pytest.mark.parametrize("key", list(LAUNCH_PLANS))
+def test_launch_plans(q8, key):
+    N, K, n_slots, ws = key
+    info = q8.q8_matmul_launch_info(N, K, n_slots, bool(ws))
+    assert tuple(info[k] for k in _PLAN_KEYS) == LAUNCH_PLANS[key]
+    # one float4 per lane, row group and column tile of every wave
+    assert info["lds_bytes"] == (info["waves_per_workgroup"] * info["row_groups_per_wave"]
+                                 * info["column_tiles"] * 64 * 16)
+
+
+def test_launch_plan_tree_does_not_depend_on_width_or_workspace(q8):
+    """The summation tree (K splits, slices per split) is the same for every
+    slot width and with or without a workspace, so a column's bits never
+    depend on how the call was made; the launch stays within 8 waves and
+    64 KB of LDS per workgroup, and a split execution exactly when the shape
+    needs a workspace."""
+    rng = __import__("random").Random(7)
+    shapes = [(34816, 5120), (5120, 17408), (18432, 7168), (7168, 18432), (17405, 1056),
+              (17981, 2080), (72003, 256), (6555, 8224), (6528, 8224), (1, 32), (17, 288)]
+    shapes += [(rng.randrange(1, 80000), 32 * rng.randrange(1, 700)) for _ in range(40)]
+    for N, K in shapes:
+        need = q8.q8_matmul_workspace_bytes(N, K)
+        plans = [q8.q8_matmul_launch_info(N, K, 16, True)]
+        plans += [q8.q8_matmul_launch_info(N, K, n, False) for n in (16, 32, 48, 64)]
+        assert len({(p["k_splits"], p["slices_per_split"]) for p in plans}) == 1, (N, K)
+        assert plans[0]["split_workgroups"] == (1 if need > 0 else 0), (N, K)
+        G = -(-N // 16)
+        for p in plans:
+            assert 1 <= p["waves_per_workgroup"] <= 8 and p["lds_bytes"] <= 64 * 1024, (N, K, p)
+            assert p["chunks_in_flight"] in (1, 2, 4)
+            rg = p["row_groups_per_wave"]
+            assert rg in (1, 2) and G >= rg
+            blocks = -(-G // rg)
+            pieces = (blocks - p["whole_row_workgroups"]) * p["k_splits"] if p["split_workgroups"] else 0
+            assert p["workgroups"] == (p["whole_row_workgroups"] + pieces if p["split_workgroups"]
+                                       else blocks), (N, K, p)
+
+
+@pytest.mark.parametrize("args", [(0, 32, 16, 0), (16, 48, 16, 0), (16, 32, 8, 0), (16, 32, 80, 0),
+                                  (16, 32, 17, 0), (16, 32, 32, 1), (16, 32, 16, 2),
+                                  (16, 32, 16, -1)])
+def test_launch_info_rejects_invalid_arguments(q8, args):
+    info = q8._LaunchInfo()
+    assert q8._lib.q8_matmul_launch_info(*args, ctypes.byref(info)) == q8.Q8_ERR_INVALID_ARG
+    assert q8._lib.q8_matmul_launch_info(16, 32, 16, 0, None) == q8.Q8_ERR_INVALID_ARG
 
 
 def test_ws_entry_point_rejects_a_missing_or_small_workspace(q8):
