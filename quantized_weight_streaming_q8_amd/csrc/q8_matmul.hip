@@ -1239,7 +1239,7 @@ Tiling choose_tiling(const Shape& s) {
             // they fill at least 80% of the CUs, one each: the 4 K ranges
             // are 4 wave slices of one workgroup, summed in LDS (the same
             // ranges in the same order as 4 splits, so the same bits), and
-            // no workspace: 18432->7168 (224 row blocks) 24.3 against 25.0 us
+            // no workspace: 18432->7168 (224 row blocks) 24.6 against 25.0-25.1 us
             t.splits = 1;
             t.kw = 4;
             t.rg_split = 2;
