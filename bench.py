@@ -1241,6 +1241,9 @@ def main(argv=None) -> int:
         "kernel": (f"fused pre-quantise + q8 narrow matmul" if args.fused else "q8 narrow matmul")
         + f", {dm.name} {dm.K}->{dm.N}, n_live={args.n_live}",
         "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 2),
+        # the launch the workspace entry point makes (the fused one adds its
+        # producer workgroups and 4 chunks in flight)
+        "launch": layer.q8.q8_matmul_launch_info(dm.N, dm.K, 16, True),
     }
 
     sweep = {}
